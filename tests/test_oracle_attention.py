@@ -1,0 +1,230 @@
+"""Pins for ``oracle.attention`` (fp64 tree-verify attention, absorbed MLA).
+
+Pinned against an independent library routine and closed forms, never
+against itself:
+
+* a chain tree equals causal extend attention over prefix + chain, and a
+  1-node tree equals plain decode attention -- both checked against
+  ``torch.nn.functional.scaled_dot_product_attention`` in float64 on the CPU
+  (the unified-forward view of "The Architecture of a Speculative Decoding
+  Engine ...", section "The Core Design Problem: A Unified Forward Pass":
+  prefill is the causal-mask case and decode the budget-0 case);
+* brute force for general trees: each node's row equals unmasked SDPA over
+  the prefix plus its materialised root path;
+* closed forms: two- and four-key cases with exact softmax weights and a
+  masked sibling that would dominate if it leaked; q = 0 gives the mean of the
+  visible c_kv rows; identical rows give that row; an empty prefix makes the
+  root attend to itself alone;
+* invariance: permuting prefix rows (slots) does not change the output;
+* mutation: wrong masks (every tree column visible, the stride-P misread, the
+  tree block shifted one column left, parents off by one, self dropped) move
+  the output by more than the parity tolerance, so the parity tests can see
+  a mask bug ("The Mask Bug That Changed Everything ...", and "The 30-Column
+  Mask ...", section "Mistakes and Incorrect Assumptions").
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, tree, visibility
+from workloads import get_config, make_workload, sensitize_tree_columns
+
+SCALE = float(np.float32(0.14468))
+DL = 512
+
+
+def _rand(seed, Q, H, P, std=0.5):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((Q, H, 576)) * std
+    kv = rng.standard_normal((P + Q, 576)) * std
+    return q, kv
+
+
+def _sdpa(q_rows, k_rows, mask=None):
+    """torch SDPA, float64, CPU: q_rows [n, H, 576], k_rows [m, 576]."""
+    n, H, _ = q_rows.shape
+    qt = torch.from_numpy(np.ascontiguousarray(q_rows.transpose(1, 0, 2)))[None]          # [1,H,n,576]
+    kt = torch.from_numpy(np.ascontiguousarray(k_rows))[None, None].expand(1, H, -1, -1)  # [1,H,m,576]
+    vt = torch.from_numpy(np.ascontiguousarray(k_rows[:, :DL]))[None, None].expand(1, H, -1, -1)
+    am = None if mask is None else torch.from_numpy(mask.astype(bool))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=am, scale=SCALE)
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+@pytest.mark.parametrize("P,Q,H", [(0, 8, 4), (21, 8, 8), (100, 5, 3)])
+def test_chain_equals_causal_extend(P, Q, H):
+    q, kv = _rand(P + Q, Q, H, P)
+    par = np.arange(-1, Q - 1)
+    out, _ = attention.verify_request(q, kv, P, par, SCALE)
+    causal = torch.ones(Q, P + Q, dtype=torch.bool).tril(P).numpy()
+    np.testing.assert_allclose(out, _sdpa(q, kv, causal), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("P", [0, 1, 30, 257])
+def test_single_node_equals_decode(P):
+    q, kv = _rand(7 + P, 1, 6, P)
+    out, lse = attention.verify_request(q, kv, P, np.array([-1]), SCALE)
+    np.testing.assert_allclose(out, _sdpa(q, kv), rtol=0, atol=1e-12)
+    s = SCALE * (q[0] @ kv.T)
+    np.testing.assert_allclose(lse[0], np.log(np.exp(s).sum(axis=1)), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed,K,B,P", [(1, 4, 8, 21), (2, 8, 32, 50), (3, 16, 64, 9), (4, 2, 20, 0)])
+def test_tree_equals_per_path_decode(seed, K, B, P):
+    rng = np.random.default_rng(seed)
+    from workloads import draw_drafter_topk
+    lp, ids = draw_drafter_topk(rng, 7, K, 512)
+    t = tree.build_tree(lp, ids, 0, B)
+    Q, H = B + 1, 4
+    q, kv = _rand(100 + seed, Q, H, P)
+    out, _ = attention.verify_request(q, kv, P, t.parents, SCALE)
+    for i in range(Q):
+        path, j = [], i
+        while j >= 0:
+            path.append(j)
+            j = int(t.parents[j])
+        rows = np.concatenate([kv[:P], kv[P + np.array(path[::-1])]])
+        np.testing.assert_allclose(out[i], _sdpa(q[i:i + 1], rows)[0], rtol=0, atol=1e-12)
+
+
+def test_two_key_closed_form():
+    a = np.log(3.0) / SCALE
+    q = np.zeros((1, 1, 576))
+    q[0, 0, 512] = a
+    kv = np.zeros((2, 576))
+    kv[0, 512] = 1.0                       # prefix row: s = ln 3
+    kv[0, :DL] = np.arange(DL) / 7.0
+    kv[1, :DL] = -1.0                      # root row: s = 0
+    out, lse = attention.verify_request(q, kv, 1, np.array([-1]), SCALE)
+    np.testing.assert_allclose(out[0, 0], 0.75 * kv[0, :DL] + 0.25 * kv[1, :DL], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], np.log(4.0), rtol=0, atol=1e-14)
+
+
+def test_masked_sibling_closed_form():
+    # prefix 1, root, two children of the root; node 2 must not see node 1,
+    # whose score would swamp everything if it leaked.
+    a = np.log(3.0) / SCALE
+    q = np.zeros((3, 1, 576))
+    q[:, 0, 512] = a
+    kv = np.zeros((4, 576))
+    kv[0, 512], kv[2, 512] = 1.0, 50.0    # a leak of node 1 would weigh e^(50 ln 3)
+    for c in range(4):
+        kv[c, :DL] = c + 1.0
+    out, lse = attention.verify_request(q, kv, 1, np.array([-1, 0, 0]), SCALE)
+    np.testing.assert_allclose(out[2, 0], np.full(DL, 0.6 * 1 + 0.2 * 2 + 0.2 * 4), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[2, 0], np.log(5.0), rtol=0, atol=1e-14)
+
+
+def test_zero_query_is_mean_of_visible_rows():
+    _, kv = _rand(5, 9, 1, 21)
+    q = np.zeros((9, 3, 576))
+    par = np.array([-1, 0, 0, 1, 1, 2, 3, 3, 7])
+    out, lse = attention.verify_request(q, kv, 21, par, SCALE)
+    m = visibility.full_mask(par, 21).astype(bool)
+    for i in range(9):
+        for h in range(3):
+            np.testing.assert_allclose(out[i, h], kv[m[i], :DL].mean(axis=0), rtol=0, atol=1e-13)
+            np.testing.assert_allclose(lse[i, h], np.log(m[i].sum()), rtol=0, atol=1e-13)
+
+
+def test_identical_rows_give_that_row():
+    q, _ = _rand(6, 5, 2, 10)
+    row = np.random.default_rng(0).standard_normal(576)
+    kv = np.tile(row, (15, 1))
+    out, _ = attention.verify_request(q, kv, 10, np.array([-1, 0, 1, 0, 3]), SCALE)
+    np.testing.assert_allclose(out, np.broadcast_to(row[:DL], out.shape), rtol=0, atol=1e-13)
+
+
+def test_empty_prefix_root_sees_itself_only():
+    q, kv = _rand(8, 4, 3, 0)
+    out, lse = attention.verify_request(q, kv, 0, np.array([-1, 0, 1, 1]), SCALE)
+    assert np.array_equal(out[0], np.broadcast_to(kv[0, :DL], (3, DL)))
+    np.testing.assert_allclose(lse[0], SCALE * (q[0] @ kv[0]), rtol=0, atol=1e-13)
+
+
+def test_prefix_permutation_invariance():
+    q, kv = _rand(9, 9, 8, 40)
+    par = np.array([-1, 0, 1, 1, 0, 4, 2, 6, 5])
+    out, lse = attention.verify_request(q, kv, 40, par, SCALE)
+    perm = np.random.default_rng(3).permutation(40)
+    kv2 = np.concatenate([kv[:40][perm], kv[40:]])
+    out2, lse2 = attention.verify_request(q, kv2, 40, par, SCALE)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# mutation: a wrong mask must move the output beyond each config's tolerance
+# ---------------------------------------------------------------------------
+def _wrong_masks(par, P):
+    Q = len(par)
+    right = visibility.full_mask(par, P)
+    out = {}
+    m = right.copy()
+    m[:, P:] = 1
+    out["all_tree_visible"] = m
+    if P > 0:
+        flat = np.concatenate([right.ravel(), np.zeros(Q * (P + Q), np.uint8)])
+        out["stride_P_misread"] = np.array([[flat[i * P + c] for c in range(P + Q)] for i in range(Q)])
+        m = right.copy()
+        m[:, P - 1:P + Q - 1] = right[:, P:]
+        m[:, P + Q - 1] = 0
+        m[:, :P - 1] = 1
+        out["tree_block_shifted_left"] = m
+    par2 = np.array([-1] + [max(0, int(p) - 1) if i >= 2 else 0 for i, p in enumerate(par[1:], 1)])
+    out["parents_off_by_one"] = visibility.full_mask(par2, P)
+    m = right.copy()
+    for i in range(1, Q):
+        m[i, P + i] = 0
+    out["self_dropped"] = m
+    for k, v in out.items():   # every row keeps at least one visible column
+        assert v.sum(axis=1).min() > 0, k
+    return right, out
+
+
+def _mutation_errors(wl, r, nodes, tol):
+    from oracle import tree as tr
+    t = tr.build_tree(wl.topk_logprobs[r], wl.topk_ids[r], int(wl.root_tokens[r]), int(wl.budgets[r]))
+    P = int(wl.prefix_lens[r])
+    a = int(wl.qo_indptr[r])
+    q = wl.q_f32()[a:a + len(t.parents)].astype(np.float64)
+    kv = wl.kv_rows_f32(wl.request_slots(r)).astype(np.float64)
+    nodes = np.arange(len(t.parents)) if nodes is None else np.array(nodes)
+    right, wrongs = _wrong_masks(t.parents, P)
+    sc = float(np.float32(wl.scale))
+    ref, _ = attention.attend(q[nodes], kv, right[nodes], sc)
+    bound = tol * np.abs(ref).max()
+    errs = {}
+    for name, m in wrongs.items():
+        bad, _ = attention.attend(q[nodes], kv, m[nodes], sc)
+        errs[name] = np.abs(bad - ref).max()
+    return errs, bound
+
+
+# (config, sampled nodes, tolerance, sensitized twin?)  The parity tests use
+# the same choice: long-context configs are checked on the sensitized twin.
+@pytest.mark.parametrize("cfg_i,nodes,tol,sens", [
+    (1, None, 1e-5, False),
+    (2, None, 1e-2, False),
+    (3, [0, 5, 17, 30, 32], 1e-2, False),
+    pytest.param(4, [3, 40, 64], 1e-2, True, marks=pytest.mark.slow),
+    pytest.param(5, [1, 9, 16], 1e-2, True, marks=pytest.mark.slow),
+])
+def test_wrong_masks_exceed_tolerance(cfg_i, nodes, tol, sens):
+    cfg = get_config(cfg_i)
+    wl = make_workload(cfg, bs=1 if cfg_i != 5 else 3, unused="zero")
+    if sens:
+        wl = sensitize_tree_columns(wl)
+    r = int(np.argmax(wl.prefix_lens))
+    errs, bound = _mutation_errors(wl, r, nodes, tol)
+    for name, err in errs.items():
+        assert err > bound, f"config {cfg_i}: mutation {name} moves output by {err:.3g} <= tol {bound:.3g}"
+
+
+@pytest.mark.slow
+def test_long_context_needs_sensitized_twin():
+    """At a 131k prefix a leaking tree mask hides inside the bf16 tolerance:
+    the reason the long-context parity test also runs the sensitized twin."""
+    wl = make_workload(get_config(4), unused="zero")
+    errs, bound = _mutation_errors(wl, 0, [3, 40, 64], 1e-2)
+    assert errs["all_tree_visible"] < bound
