@@ -1,0 +1,232 @@
+/*
+ * ddtree.h -- C ABI of libddtree.so: the DDTree tree-verify hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Four stages of one speculative verify step, in the order a caller runs them:
+ *   ddtree_build_tree          best-first draft tree from per-depth top-k log-probs
+ *   ddtree_compile_visibility  ancestor-or-self bitsets (+ positions, + dense mask)
+ *   ddtree_verify_attn         absorbed-MLA attention of every tree node x head
+ *                              over the shared prefix plus its own ancestors
+ *   ddtree_accept              greedy walk along the target argmax
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array argument is a DEVICE pointer owned by the caller (e.g. a
+ *    torch tensor's storage).  The library never allocates, frees or
+ *    synchronises; each call only enqueues kernels on `stream` (a
+ *    hipStream_t; NULL = the default stream) and returns.  No call reads
+ *    device memory on the host, so all calls can be captured in a HIP graph.
+ *  - Requests are packed ragged: request r owns tree nodes
+ *    [qo_indptr[r], qo_indptr[r+1]); its q_len Q_r = budget_r + 1 (root +
+ *    budget draft nodes).  Node indices inside a request are request-local
+ *    (root = 0).  qo_indptr must be computed from the budgets -- never from
+ *    the drafter block size, which misaligned every offset whenever
+ *    budget + 1 != block_size ("The Mask Bug That Changed Everything: A
+ *    Post-Mortem on DDTree Speculative Decoding", section "The Context: A
+ *    Cascade of Infrastructure and Algorithm Challenges").
+ *  - Host-known scalars (bs, max_q_len, max_budget, words_per_row, ...) size
+ *    the launch; device data is trusted to agree with them.  Device data that
+ *    disagrees never makes a kernel read or write out of bounds, but the
+ *    affected outputs are unspecified (see each call).
+ *  - Return value: DDTREE_OK, or a negative ddtree_status_t when the host
+ *    arguments are invalid (nothing is enqueued then) or a launch failed.
+ *    ddtree_last_error() gives a message for the calling thread.
+ *    Asynchronous device faults surface at the caller's next synchronisation.
+ */
+#ifndef DDTREE_H
+#define DDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDTREE_ABI_VERSION 1
+
+typedef enum {
+  DDTREE_OK = 0,
+  DDTREE_EINVAL = -1,       /* invalid host argument                          */
+  DDTREE_EUNSUPPORTED = -2, /* valid but outside what this build supports     */
+  DDTREE_EWORKSPACE = -3,   /* workspace missing or smaller than required     */
+  DDTREE_EHIP = -4          /* a HIP runtime call or kernel launch failed     */
+} ddtree_status_t;
+
+typedef enum { DDTREE_F32 = 0, DDTREE_BF16 = 1 } ddtree_dtype_t;
+
+/* DDTREE_ABI_VERSION of the loaded library. */
+int ddtree_abi_version(void);
+
+/* Message for the calling thread's last non-OK return ("" if none). */
+const char* ddtree_last_error(void);
+
+/*
+ * ddtree_build_tree -- best-first growth of each request's draft tree.
+ *
+ * Defined by "The DDTree CUDA Graph Fix: Unlocking Speculative Decoding at
+ * 109 tok/s on PCIe Blackwell", section "The DDTree Architecture: Confirming
+ * Multiple-Path Evaluation": the candidate with the highest cumulative
+ * log-prob is taken and added to the tree, its best child and next-ranked
+ * sibling become candidates, until budget draft nodes are in the tree.  The
+ * root (node 0) is the last verified token ("The Oracle Drafter: Validating
+ * a Custom DDTree Speculative Decoding Engine", section "The Engine
+ * Interface Design").
+ *
+ *   topk_logprobs  [bs, depth_max, topk] f32: row d holds the top-k log-probs
+ *                  of draft depth d+1, non-increasing, all <= 0.
+ *   topk_ids       [bs, depth_max, topk] i32: matching token ids.
+ *   root_tokens    [bs] i32.
+ *   qo_indptr      [bs+1] i32: budget_r = qo_indptr[r+1] - qo_indptr[r] - 1.
+ *   max_budget     host bound on every budget_r; must satisfy
+ *                  max_budget <= sum_{d=1..depth_max} topk^d.
+ *   Outputs, packed by qo_indptr: node_tokens, node_parents (root -1,
+ *   otherwise a smaller request-local index), node_depths (root 0) as i32;
+ *   node_scores f32 cumulative log-prob (root 0), nullable.
+ *
+ * Node order is pop order.  Scores are accumulated in fp32 root to leaf as
+ * f32(parent_score + lp); ties in score go to the smaller depth, then to the
+ * lexicographically smaller rank path.  Results are bit-exact.
+ * Errors: EINVAL (null pointer, bs < 0, max_budget < 0, depth_max/topk < 1
+ * with max_budget > 0, max_budget unreachable); EUNSUPPORTED when
+ * depth_max * ceil(log2(topk)) > 64 (rank paths are packed in 64 bits).
+ * A request whose budget exceeds max_budget gets only max_budget draft nodes;
+ * its remaining node slots are written as token -1, parent -1, depth -1.
+ */
+int ddtree_build_tree(const float* topk_logprobs, const int32_t* topk_ids,
+                      const int32_t* root_tokens, const int32_t* qo_indptr, int bs,
+                      int depth_max, int topk, int max_budget, int32_t* node_tokens,
+                      int32_t* node_parents, int32_t* node_depths, float* node_scores,
+                      void* stream);
+
+/*
+ * ddtree_compile_visibility -- ancestor-or-self bitsets of every tree node.
+ *
+ * Defined by "The DDTree CUDA Graph Fix ...", section "The DDTree
+ * Architecture: Confirming Multiple-Path Evaluation" (each node attends only
+ * to its ancestors plus the shared prefix), "The Architecture of a
+ * Speculative Decoding Engine: Designing KV Cache Semantics for DDTree
+ * Inference", section "The Final Resolution: A Concrete Trace" (the root
+ * sits at position = cache length and sees itself; a depth-d node sits d
+ * positions later), and "The 30-Column Mask: Debugging a Structural
+ * Marshaling Mismatch in Custom MLA Verification Attention", section "Mask
+ * Stride Formula" (the flattened mask is [q_len, prefix_len + q_len]
+ * row-major, prefix columns first).
+ *
+ *   node_parents, node_depths  [total_q] i32 as written by ddtree_build_tree.
+ *   qo_indptr [bs+1] i32, prefix_lens [bs] i32 (P_r >= 0).
+ *   words_per_row  W >= ceil(max_q_len / 32).
+ *   vis_bits   [total_q, W] u32: bit (j % 32) of word j / 32 is set iff node j
+ *              of the same request is the row's node or one of its ancestors.
+ *   positions  nullable [total_q] i64: P_r + depth.
+ *   dense_mask nullable u8, with mask_indptr [bs+1] i64 (both or neither):
+ *              request r's rows start at dense_mask + mask_indptr[r], row i is
+ *              P_r ones followed by the row's Q_r visibility bits as bytes
+ *              (stride P_r + Q_r).
+ * Errors: EINVAL (null required pointer, bs < 0, max_q_len < 1 with bs > 0,
+ * W too small, only one of dense_mask / mask_indptr given).  A parent that is
+ * not a smaller index ends that row's ancestor walk.
+ */
+int ddtree_compile_visibility(const int32_t* node_parents, const int32_t* node_depths,
+                              const int32_t* qo_indptr, const int32_t* prefix_lens, int bs,
+                              int max_q_len, int words_per_row, uint32_t* vis_bits,
+                              int64_t* positions, uint8_t* dense_mask,
+                              const int64_t* mask_indptr, void* stream);
+
+/*
+ * ddtree_verify_attn_workspace_size -- bytes of device workspace that
+ * ddtree_verify_attn needs for these sizes on the current device (0 if none).
+ * The count depends on the current device's compute-unit count when
+ * num_splits == 0.  Returns 0 for invalid sizes.
+ */
+size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int max_q_len, int max_kv_len,
+                                         int num_splits, int dtype);
+
+/*
+ * ddtree_verify_attn -- tree-verify attention, absorbed MLA.
+ *
+ * Defined by "The Architecture of a Speculative Decoding Engine ...",
+ * section "The Forward Pass Pseudocode" (attention of the absorbed query and
+ * roped query part over the cached c_kv and k_pe under a mask, output in
+ * latent space), "The 30-Column Mask ...", sections "The Message: Tensor
+ * Shapes as Evidence" and "The Fix: Building Combined Indices" (576-wide
+ * latent rows = 512 c_kv + 64 rope in a slot pool; each request's KV list is
+ * its prefix slots followed by the slots of its tree nodes; the mask stride
+ * is prefix_len + q_len) and "The DDTree CUDA Graph Fix ...", section "The
+ * DDTree Architecture: Confirming Multiple-Path Evaluation" (all nodes in
+ * one pass; the prefix is read once for all of them).
+ *
+ *   q          [total_q, H, 576] dtype: cols 0..511 absorbed q_nope, 512..575
+ *              roped q_pe; rows node-major, head-minor.
+ *   kv_pool    [num_slots, 576] dtype: cols 0..511 c_kv, 512..575 k_pe.
+ *   kv_indptr  [bs+1] i32 and kv_indices i32: request r's logical columns
+ *              c = 0 .. N_r-1 (N_r = kv_indptr[r+1] - kv_indptr[r]) read pool
+ *              row kv_indices[kv_indptr[r] + c].  The first P_r = N_r - Q_r
+ *              are prefix slots, the last Q_r the tree nodes' own slots in
+ *              node order.
+ *   qo_indptr  [bs+1] i32; vis_bits [total_q, words_per_row] u32 as written
+ *              by ddtree_compile_visibility.
+ *   max_q_len  >= every Q_r; max_kv_len >= every N_r (host bounds).
+ *   scale      softmax scale on the full 576-d dot product.
+ *   out        [total_q, H, 512] dtype: sum over visible columns of
+ *              softmax(scale * q . kv) * c_kv.
+ *   lse        nullable [total_q, H] f32: natural-log log-sum-exp of the
+ *              scaled scores.
+ *   num_splits 0 = automatic (bf16: persistent work split evenly over the
+ *              device's compute units, partial results merged by log-sum-exp;
+ *              f32: no split); S >= 1 = each row tile's KV range cut into S
+ *              equal parts, then merged.  The result does not depend on the
+ *              split beyond rounding.
+ *   workspace  device scratch of at least ddtree_verify_attn_workspace_size()
+ *              bytes (may be NULL when that is 0).
+ * Arithmetic: bf16 inputs use bf16 matrix cores with fp32 accumulation, the
+ * softmax weights rounded to bf16 for the value product, output rounded to
+ * bf16; f32 inputs compute in fp32 throughout.
+ * Errors: EINVAL (null required pointer, bs < 0, num_heads < 1, max_q_len < 1,
+ * max_kv_len < max_q_len, words_per_row too small, non-finite scale,
+ * num_slots < 1, num_splits < 0, bad dtype); EWORKSPACE.  A pool index
+ * outside [0, num_slots) is clamped into range (a valid row is read); a
+ * request with N_r < Q_r is skipped (its outputs are left untouched).
+ */
+int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t num_slots,
+                       const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* qo_indptr, const uint32_t* vis_bits, int words_per_row,
+                       int bs, int num_heads, int max_q_len, int max_kv_len, float scale,
+                       int dtype, void* out, float* lse, int num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * ddtree_accept -- greedy acceptance along the target argmax.
+ *
+ * Defined by "The DDTree CUDA Graph Fix ...", section "The DDTree
+ * Architecture: Confirming Multiple-Path Evaluation" (walk from the root,
+ * stepping to the child whose token equals the target's argmax at the
+ * current node, until none matches; the longest chain plus one bonus token),
+ * "The Oracle Drafter ...", section "The Engine Interface Design" (outputs:
+ * accepted path, accept length, proposed tokens, bonus) and "The
+ * Architecture of a Speculative Decoding Engine ...", section "The Final
+ * Resolution: A Concrete Trace" (the accepted nodes, root included, are
+ * committed; autoregressive decoding is the budget-0 case, accept length 1).
+ *
+ *   node_tokens, node_parents [total_q] i32; qo_indptr [bs+1] i32;
+ *   target_predict [total_q] i32: target argmax at every node.
+ *   depth_max  D: the walk stops after D + 1 path nodes.
+ *   accepted_nodes [bs, D+1] i32: request-local path, root first, -1 padded.
+ *   accept_len     [bs] i32 in 1..D+1 (counts the root).
+ *   commit_tokens  [bs, D+1] i32: the accepted draft tokens then the bonus
+ *                  (accept_len tokens), -1 padded.
+ *   bonus_tokens   [bs] i32: target argmax at the last accepted node.
+ * If two children of one node carry the same token the smaller index wins.
+ * Errors: EINVAL (null pointer, bs < 0, depth_max < 0).  A request with
+ * Q_r < 1 gets accept_len 0 and all -1 rows.
+ */
+int ddtree_accept(const int32_t* node_tokens, const int32_t* node_parents,
+                  const int32_t* qo_indptr, const int32_t* target_predict, int bs, int depth_max,
+                  int32_t* accepted_nodes, int32_t* accept_len, int32_t* commit_tokens,
+                  int32_t* bonus_tokens, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDTREE_H */

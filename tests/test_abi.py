@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/ddtree.h declares, and rejects invalid host arguments with the
+documented status codes before touching the device."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from tree_verify_mla_amd import _lib
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "ddtree.h"
+
+EINVAL, EUNSUPPORTED, EWORKSPACE = -1, -2, -3
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddtree_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_stages():
+    names = declared_functions()
+    for n in ("ddtree_build_tree", "ddtree_compile_visibility", "ddtree_verify_attn", "ddtree_accept"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} missing from libddtree.so"
+
+
+def test_abi_version(lib):
+    assert lib.ddtree_abi_version() == 1
+
+
+def _err(lib):
+    return lib.ddtree_last_error().decode()
+
+
+def test_build_tree_validation(lib):
+    f = lib.ddtree_build_tree
+    assert f(FAKE, FAKE, FAKE, FAKE, -1, 7, 4, 8, FAKE, FAKE, FAKE, NULL, NULL) == EINVAL
+    assert f(FAKE, FAKE, NULL, FAKE, 1, 7, 4, 8, FAKE, FAKE, FAKE, NULL, NULL) == EINVAL
+    # 1 + 1 = 2 rank paths reachable with depth 2, top-1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 3, FAKE, FAKE, FAKE, NULL, NULL) == EINVAL
+    assert "reachable" in _err(lib)
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 4, 3, FAKE, FAKE, FAKE, NULL, NULL) == EINVAL
+    # rank paths must pack into 64 bits: depth 20 x 8 bits (top-256) does not
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 20, 256, 8, FAKE, FAKE, FAKE, NULL, NULL) == EUNSUPPORTED
+    assert f(NULL, NULL, NULL, NULL, 0, 7, 4, 8, NULL, NULL, NULL, NULL, NULL) == 0  # empty batch
+
+
+def test_visibility_validation(lib):
+    f = lib.ddtree_compile_visibility
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 33, 1, FAKE, NULL, NULL, NULL, NULL) == EINVAL  # W too small
+    assert "words_per_row" in _err(lib)
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 33, 2, FAKE, NULL, FAKE, NULL, NULL) == EINVAL  # mask w/o indptr
+    assert f(NULL, FAKE, FAKE, FAKE, 2, 33, 2, FAKE, NULL, NULL, NULL, NULL) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 0, 2, FAKE, NULL, NULL, NULL, NULL) == EINVAL
+
+
+def _attn(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, num_slots=100, kvp=FAKE, kvi=FAKE, qo=FAKE, vis=FAKE, W=2, bs=1, H=8,
+             max_q=33, max_kv=100, scale=0.14468, dtype=_lib.DDTREE_F32, out=FAKE, lse=NULL,
+             splits=1, ws=NULL, ws_bytes=0)
+    a.update(kw)
+    return lib.ddtree_verify_attn(a["q"], a["kv"], a["num_slots"], a["kvp"], a["kvi"], a["qo"],
+                                  a["vis"], a["W"], a["bs"], a["H"], a["max_q"], a["max_kv"],
+                                  a["scale"], a["dtype"], a["out"], a["lse"], a["splits"], a["ws"],
+                                  a["ws_bytes"], NULL)
+
+
+def test_verify_attn_validation(lib):
+    assert _attn(lib, bs=-1) == EINVAL
+    assert _attn(lib, q=NULL) == EINVAL
+    assert _attn(lib, H=0) == EINVAL
+    assert _attn(lib, max_kv=10) == EINVAL          # max_kv_len < max_q_len
+    assert _attn(lib, W=1) == EINVAL                # 32 bits cannot cover 33 nodes
+    assert _attn(lib, scale=float("nan")) == EINVAL
+    assert _attn(lib, num_slots=0) == EINVAL
+    assert _attn(lib, splits=-1) == EINVAL
+    assert _attn(lib, dtype=7) == EINVAL
+    assert _attn(lib, splits=4, ws=NULL, ws_bytes=0) == EWORKSPACE
+    assert "workspace" in _err(lib)
+    assert _attn(lib, bs=0) == 0
+
+
+def test_workspace_size_forced_split(lib):
+    # fp32 tiles hold 4 rows; 33 nodes x 8 heads = 264 rows -> 66 tiles
+    per_slot = 4 * (512 + 2) * 4
+    assert lib.ddtree_verify_attn_workspace_size(2, 8, 33, 100, 3, _lib.DDTREE_F32) == 2 * 66 * 3 * per_slot
+    assert lib.ddtree_verify_attn_workspace_size(2, 8, 33, 100, 1, _lib.DDTREE_F32) == 0
+    assert lib.ddtree_verify_attn_workspace_size(2, 8, 33, 100, 0, _lib.DDTREE_F32) == 0
+    # bf16 tiles hold 64 rows -> 5 tiles
+    assert lib.ddtree_verify_attn_workspace_size(1, 8, 33, 100, 2, _lib.DDTREE_BF16) == 5 * 2 * 64 * 514 * 4
+    assert lib.ddtree_verify_attn_workspace_size(-1, 8, 33, 100, 2, _lib.DDTREE_BF16) == 0
+
+
+def test_accept_validation(lib):
+    f = lib.ddtree_accept
+    assert f(FAKE, FAKE, FAKE, FAKE, -1, 7, FAKE, FAKE, FAKE, FAKE, NULL) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, -1, FAKE, FAKE, FAKE, FAKE, NULL) == EINVAL
+    assert f(FAKE, NULL, FAKE, FAKE, 1, 7, FAKE, FAKE, FAKE, FAKE, NULL) == EINVAL
+    assert f(NULL, NULL, NULL, NULL, 0, 7, NULL, NULL, NULL, NULL, NULL) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        _lib.ddtree_accept(t, t, t, t, 7, t, t, t, t)

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: tree, visibility, positions, dense mask and accept bit-exact;
+attention max|err| <= 1e-2 * max|out| for bf16 and <= 1e-5 * max|out| for
+fp32; lse within 2e-3 (bf16) / 1e-5 (fp32) absolute.  Small workloads are
+compared on every output; the full-size configurations run in the bench's
+launch configuration (persistent split, num_splits = 0) and are compared on
+sampled nodes (root, middle, last of each request, all heads).  Long-context
+configurations are also run on their sensitized twin, where a mask error
+would exceed the tolerance (tests/test_oracle_attention.py shows a leak is
+invisible at 131k prefix otherwise).  Unused pool rows are NaN, so a stray
+read poisons the output.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from tests._oracle_side import OracleRun, sample_nodes
+from tree_verify_mla_amd import _lib
+from tree_verify_mla_amd.step import VerifyStep
+from workloads import get_config, make_workload, sensitize_tree_columns
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-5}
+LSE_TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(wl, num_splits=0):
+    orc = OracleRun(wl)
+    x = to_device(wl, "cuda", target_predict=orc.target_predict)
+    st = VerifyStep(x, num_splits=num_splits)
+    st.run()
+    torch.cuda.synchronize()
+    return orc, st
+
+
+def _out_f64(st):
+    return st.out.float().cpu().numpy().astype(np.float64)
+
+
+def _check_integer_stages(orc, st):
+    assert np.array_equal(st.node_tokens.cpu().numpy(), orc.tokens)
+    assert np.array_equal(st.node_parents.cpu().numpy(), orc.parents)
+    assert np.array_equal(st.node_depths.cpu().numpy(), orc.depths)
+    assert np.array_equal(st.node_scores.cpu().numpy().view(np.uint32), orc.scores.view(np.uint32))
+    assert np.array_equal(st.vis_bits.cpu().numpy().view(np.uint32), orc.bits)
+    assert np.array_equal(st.positions.cpu().numpy(), orc.positions)
+    nodes, alen, commit, bonus = orc.accept
+    assert np.array_equal(st.accepted_nodes.cpu().numpy(), nodes)
+    assert np.array_equal(st.accept_len.cpu().numpy(), alen)
+    assert np.array_equal(st.commit_tokens.cpu().numpy(), commit)
+    assert np.array_equal(st.bonus_tokens.cpu().numpy(), bonus)
+
+
+def _check_attention(orc, st, sampled: bool):
+    wl = orc.wl
+    out = _out_f64(st)
+    lse = st.lse.cpu().numpy().astype(np.float64)
+    worst, worst_lse = 0.0, 0.0
+    for r in range(wl.bs):
+        a, b = int(wl.qo_indptr[r]), int(wl.qo_indptr[r + 1])
+        nodes = sample_nodes(b - a) if sampled else list(range(b - a))
+        ref, ref_lse = orc.attention_rows(r, nodes)
+        got = out[a + np.array(nodes)]
+        assert np.isfinite(got).all(), f"request {r}: non-finite output"
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        worst = max(worst, err)
+        worst_lse = max(worst_lse, np.abs(lse[a + np.array(nodes)] - ref_lse).max())
+    _say(f"  {wl.name}: max|err|/max|out| = {worst:.3e}, max|lse err| = {worst_lse:.3e}")
+    assert worst <= TOL[wl.dtype]
+    assert worst_lse <= LSE_TOL[wl.dtype]
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 3])
+def test_c1_tiny_fp32(num_splits):
+    _say(f"test_c1_tiny_fp32 splits={num_splits}")
+    orc, st = _run(make_workload(get_config(1)), num_splits)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st, sampled=False)
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 2])
+def test_c1_shape_bf16(num_splits):
+    _say(f"test_c1_shape_bf16 splits={num_splits}")
+    orc, st = _run(make_workload(get_config(1), dtype="bf16"), num_splits)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st, sampled=False)
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 7])
+def test_c2_shard_bf16_full_compare(num_splits):
+    _say(f"test_c2 splits={num_splits}")
+    orc, st = _run(make_workload(get_config(2)), num_splits)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st, sampled=False)
+
+
+def test_ragged_edges_bf16():
+    """Empty and odd prefixes, budget 0 (autoregressive), ragged tails across tiles."""
+    _say("test_ragged_edges_bf16")
+    wl = make_workload(get_config(3), bs=6, heads=16, budgets=[0, 1, 8, 16, 64, 33],
+                       prefixes=[0, 1, 31, 33, 700, 5000], pool_slots=20000)
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st, sampled=False)
+    for S in (1, 5):
+        orc2, st2 = _run(wl, S)
+        _check_attention(orc2, st2, sampled=False)
+
+
+def test_ragged_edges_fp32():
+    _say("test_ragged_edges_fp32")
+    wl = make_workload(get_config(1), bs=4, heads=3, budgets=[0, 5, 8, 31], prefixes=[0, 2, 33, 100],
+                       pool_slots=400)
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st, sampled=False)
+
+
+def test_c3_headline_full_size_sampled():
+    _say("test_c3_headline_full_size_sampled")
+    orc, st = _run(make_workload(get_config(3)))
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st, sampled=True)
+
+
+@pytest.mark.parametrize("twin", [False, True])
+def test_c4_long_context_sampled(twin):
+    _say(f"test_c4_long_context_sampled twin={twin}")
+    wl = make_workload(get_config(4))
+    if twin:
+        wl = sensitize_tree_columns(wl)
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st, sampled=True)
+
+
+def test_c4_forced_splits_agree():
+    """Split count must not change the result beyond rounding."""
+    _say("test_c4_forced_splits_agree")
+    wl = sensitize_tree_columns(make_workload(get_config(4)))
+    orc, st = _run(wl, num_splits=64)
+    _check_attention(orc, st, sampled=True)
+
+
+@pytest.mark.parametrize("twin", [False, True])
+def test_c5_ragged_e2e_sampled(twin):
+    _say(f"test_c5_ragged_e2e_sampled twin={twin}")
+    wl = make_workload(get_config(5))
+    if twin:
+        wl = sensitize_tree_columns(wl)
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st, sampled=True)
+
+
+def test_dense_mask_matches_oracle():
+    _say("test_dense_mask_matches_oracle")
+    wl = make_workload(get_config(3), bs=3, heads=2, budgets=[8, 32, 64], prefixes=[21, 0, 333],
+                       pool_slots=2000)
+    orc = OracleRun(wl)
+    x = to_device(wl, "cuda")
+    st = VerifyStep(x)
+    st.build()
+    mi = orc.mask_indptr()
+    dense = torch.full((int(mi[-1]),), 7, dtype=torch.uint8, device="cuda")
+    _lib.ddtree_compile_visibility(st.node_parents, st.node_depths, x.qo_indptr, x.prefix_lens,
+                                   x.max_q_len, st.vis_bits, positions=st.positions,
+                                   dense_mask=dense,
+                                   mask_indptr=torch.from_numpy(mi).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(dense.cpu().numpy(), orc.dense)
+
+
+def test_build_tree_exact_many_shapes():
+    """Bit-exact trees over depth/top-k/budget combinations, incl. ties."""
+    _say("test_build_tree_exact_many_shapes")
+    for (D, K, budgets) in [(7, 4, [8, 0, 3]), (7, 8, [32, 16, 64]), (7, 16, [64, 1, 40]),
+                            (3, 2, [14, 7, 1]), (1, 5, [5, 2, 0])]:
+        wl = make_workload(get_config(3), bs=3, heads=1, depth=D, topk=K, budgets=budgets,
+                           prefixes=[4, 4, 4], pool_slots=400, seed=77 + D * K)
+        # coarse log-probs give exact fp32 ties in the scores
+        lp = np.minimum(0, np.round(wl.topk_logprobs * 2) / 2).astype(np.float32)
+        wl.topk_logprobs = -np.sort(-lp, axis=2)
+        orc = OracleRun(wl)
+        x = to_device(wl, "cuda")
+        st = VerifyStep(x)
+        st.build()
+        torch.cuda.synchronize()
+        assert np.array_equal(st.node_tokens.cpu().numpy(), orc.tokens), (D, K)
+        assert np.array_equal(st.node_parents.cpu().numpy(), orc.parents), (D, K)
+        assert np.array_equal(st.node_depths.cpu().numpy(), orc.depths), (D, K)
+
+
+def test_accept_sentinel_and_full_chain():
+    _say("test_accept_sentinel_and_full_chain")
+    wl = make_workload(get_config(3), bs=2, heads=1, budgets=[32, 32], prefixes=[4, 4], pool_slots=200)
+    orc = OracleRun(wl)
+    x = to_device(wl, "cuda")
+    st = VerifyStep(x)
+    st.build()
+    from oracle import accept as oacc
+    # request 0: sentinel everywhere; request 1: follow the best path to the deepest node
+    tok, par = orc.tokens, orc.parents
+    pred = np.full(len(tok), -1, np.int32)
+    a = int(wl.qo_indptr[1])
+    t1 = orc.trees[1]
+    deepest = int(np.argmax(t1.depths))
+    path, j = [], deepest
+    while j >= 0:
+        path.append(j)
+        j = int(t1.parents[j])
+    path.reverse()
+    for u, v in zip(path[:-1], path[1:]):
+        pred[a + u] = t1.tokens[v]
+    pred[a + deepest] = 4242
+    tp = torch.from_numpy(pred).cuda()
+    st.accept(target_predict=tp)
+    torch.cuda.synchronize()
+    ref = oacc.batch(tok, par, wl.qo_indptr, pred, wl.depth)
+    assert np.array_equal(st.accept_len.cpu().numpy(), ref[1])
+    assert st.accept_len.cpu().numpy().tolist() == [1, len(path)]
+    assert np.array_equal(st.commit_tokens.cpu().numpy(), ref[2])
+    assert st.bonus_tokens.cpu().numpy().tolist() == [-1, 4242]
+
+
+def test_graph_replay_matches_eager():
+    """The whole step captured in one graph, replayed with eager work between."""
+    _say("test_graph_replay_matches_eager")
+    wl = make_workload(get_config(2))
+    orc = OracleRun(wl)
+    x = to_device(wl, "cuda", target_predict=orc.target_predict)
+    st = VerifyStep(x)
+    st.run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (st.node_tokens, st.vis_bits, st.out, st.lse, st.commit_tokens)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        st.run(stream=s)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        st.run(stream=s)
+    for rep in range(4):
+        for t in (st.node_tokens, st.vis_bits, st.out, st.lse, st.commit_tokens):
+            t.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for a, b in zip(eager, (st.node_tokens, st.vis_bits, st.out, st.lse, st.commit_tokens)):
+            assert torch.equal(a, b), f"replay {rep} differs from eager"

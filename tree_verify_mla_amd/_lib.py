@@ -1,0 +1,148 @@
+"""ctypes binding of libddtree.so (declared in include/ddtree.h).
+
+Argument marshalling only: every function checks that the tensors it is
+handed are contiguous device tensors of the expected dtype, passes their
+device pointers and the current torch stream to the C entry point of the
+same name, and raises ``DDTreeError`` on a non-zero status.  All arithmetic
+happens in the library's HIP kernels; outputs are written into the tensors
+the caller provides.  There is no fallback: if the library is missing,
+loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+LIB_PATH = Path(__file__).with_name("libddtree.so")
+
+DDTREE_F32 = 0
+DDTREE_BF16 = 1
+STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
+
+_lib = None
+
+
+class DDTreeError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load libddtree.so (built in-tree by ``python -m tree_verify_mla_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m tree_verify_mla_amd.build`")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.ddtree_abi_version.restype = I
+    lib.ddtree_abi_version.argtypes = []
+    lib.ddtree_last_error.restype = ctypes.c_char_p
+    lib.ddtree_last_error.argtypes = []
+    lib.ddtree_build_tree.restype = I
+    lib.ddtree_build_tree.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P]
+    lib.ddtree_compile_visibility.restype = I
+    lib.ddtree_compile_visibility.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P]
+    lib.ddtree_verify_attn_workspace_size.restype = SZ
+    lib.ddtree_verify_attn_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.ddtree_verify_attn.restype = I
+    lib.ddtree_verify_attn.argtypes = [P, P, I64, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P, SZ, P]
+    lib.ddtree_accept.restype = I
+    lib.ddtree_accept.argtypes = [P, P, P, P, I, I, P, P, P, P, P]
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise DDTreeError(fn, rc, load().ddtree_last_error().decode(errors="replace"))
+
+
+def _p(t: Optional[torch.Tensor], dtype=None, name: str = "tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def ddtree_abi_version() -> int:
+    return load().ddtree_abi_version()
+
+
+def ddtree_build_tree(topk_logprobs, topk_ids, root_tokens, qo_indptr, max_budget: int,
+                      node_tokens, node_parents, node_depths, node_scores=None, stream=None):
+    bs, D, K = topk_logprobs.shape
+    _check("ddtree_build_tree", load().ddtree_build_tree(
+        _p(topk_logprobs, torch.float32, "topk_logprobs"), _p(topk_ids, torch.int32, "topk_ids"),
+        _p(root_tokens, torch.int32, "root_tokens"), _p(qo_indptr, torch.int32, "qo_indptr"),
+        bs, D, K, int(max_budget), _p(node_tokens, torch.int32, "node_tokens"),
+        _p(node_parents, torch.int32, "node_parents"), _p(node_depths, torch.int32, "node_depths"),
+        _p(node_scores, torch.float32, "node_scores"), _stream(stream)))
+
+
+def ddtree_compile_visibility(node_parents, node_depths, qo_indptr, prefix_lens, max_q_len: int,
+                              vis_bits, positions=None, dense_mask=None, mask_indptr=None,
+                              stream=None):
+    bs = qo_indptr.numel() - 1
+    W = vis_bits.shape[1]
+    _check("ddtree_compile_visibility", load().ddtree_compile_visibility(
+        _p(node_parents, torch.int32, "node_parents"), _p(node_depths, torch.int32, "node_depths"),
+        _p(qo_indptr, torch.int32, "qo_indptr"), _p(prefix_lens, torch.int32, "prefix_lens"),
+        bs, int(max_q_len), W, _p(vis_bits, torch.int32, "vis_bits"),
+        _p(positions, torch.int64, "positions"), _p(dense_mask, torch.uint8, "dense_mask"),
+        _p(mask_indptr, torch.int64, "mask_indptr"), _stream(stream)))
+
+
+def ddtree_verify_attn_workspace_size(bs: int, num_heads: int, max_q_len: int, max_kv_len: int,
+                                      num_splits: int, dtype: int) -> int:
+    return int(load().ddtree_verify_attn_workspace_size(bs, num_heads, max_q_len, max_kv_len,
+                                                        num_splits, dtype))
+
+
+def ddtree_verify_attn(q, kv_pool, kv_indptr, kv_indices, qo_indptr, vis_bits, max_q_len: int,
+                       max_kv_len: int, scale: float, out, lse=None, num_splits: int = 0,
+                       workspace=None, stream=None):
+    if q.dtype == torch.bfloat16:
+        dt = DDTREE_BF16
+    elif q.dtype == torch.float32:
+        dt = DDTREE_F32
+    else:
+        raise TypeError("q must be bfloat16 or float32")
+    total_q, H, width = q.shape
+    bs = qo_indptr.numel() - 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("ddtree_verify_attn", load().ddtree_verify_attn(
+        _p(q, q.dtype, "q"), _p(kv_pool, q.dtype, "kv_pool"), int(kv_pool.shape[0]),
+        _p(kv_indptr, torch.int32, "kv_indptr"), _p(kv_indices, torch.int32, "kv_indices"),
+        _p(qo_indptr, torch.int32, "qo_indptr"), _p(vis_bits, torch.int32, "vis_bits"),
+        vis_bits.shape[1], bs, H, int(max_q_len), int(max_kv_len), float(scale), dt,
+        _p(out, q.dtype, "out"), _p(lse, torch.float32, "lse"), int(num_splits),
+        _p(workspace, None, "workspace"), ws_bytes, _stream(stream)))
+
+
+def ddtree_accept(node_tokens, node_parents, qo_indptr, target_predict, depth_max: int,
+                  accepted_nodes, accept_len, commit_tokens, bonus_tokens, stream=None):
+    bs = qo_indptr.numel() - 1
+    _check("ddtree_accept", load().ddtree_accept(
+        _p(node_tokens, torch.int32, "node_tokens"), _p(node_parents, torch.int32, "node_parents"),
+        _p(qo_indptr, torch.int32, "qo_indptr"), _p(target_predict, torch.int32, "target_predict"),
+        bs, int(depth_max), _p(accepted_nodes, torch.int32, "accepted_nodes"),
+        _p(accept_len, torch.int32, "accept_len"), _p(commit_tokens, torch.int32, "commit_tokens"),
+        _p(bonus_tokens, torch.int32, "bonus_tokens"), _stream(stream)))

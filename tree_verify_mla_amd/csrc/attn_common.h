@@ -1,0 +1,166 @@
+// Work decomposition shared by the verify-attention kernels and the merge.
+//
+// Request r has R_r = Q_r * H query rows (node-major, head-minor) and
+// N_r = P_r + Q_r logical KV columns.  Rows are cut into tiles of `mt` rows,
+// columns into blocks of KB.  One work unit = (row tile, KV block).
+//
+// Two schedules:
+//  * persistent (num_splits == 0): the grid's G workgroups take equal
+//    contiguous ranges of the global unit list (requests in order, tiles in
+//    order, blocks fastest).  A workgroup's range is a sequence of segments,
+//    each inside one tile; a segment that covers its whole tile writes the
+//    final output, any other writes a partial (unnormalised O, running max,
+//    running sum) into workspace slot 2*w + (first segment of w ? 0 : 1).
+//    Small problems use fewer workgroups (at least MIN_UNITS units each).
+//  * split (num_splits == S >= 1): workgroup (r, t, s) takes blocks
+//    [s*NB/S, (s+1)*NB/S) of tile t; S == 1 writes final output, S > 1
+//    writes slot (r * T_max + t) * S + s.
+// The merge kernel combines a tile's partials by log-sum-exp ("The 30-Column
+// Mask ...", section "The Context: Building a Custom Verify Attention
+// Kernel": KV-split flash decoding with a partial reduction).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ddtree {
+namespace attn {
+
+constexpr int LATENT = 576;
+constexpr int DV = 512;
+constexpr int KB = 32;          // KV columns per work unit
+constexpr int MIN_UNITS = 8;    // smallest persistent range per workgroup
+constexpr int MT_BF16 = 64;     // rows per tile, bf16 matrix-core kernel (4 waves: 2 pairs x 2 halves)
+constexpr int MT_F32 = 4;       // rows per tile, fp32 kernel
+
+struct Params {
+  const void* q;
+  const void* pool;
+  long long num_slots;
+  const int32_t* kvp;
+  const int32_t* kvi;
+  const int32_t* qo;
+  const uint32_t* vis;
+  int W;
+  int bs;
+  int H;
+  int T_max;      // tiles per request upper bound (from max_q_len)
+  int S;          // 0 = persistent schedule, else forced split count
+  float scale_log2;
+  void* out;
+  float* lse;
+  float* ws;      // partial slots
+};
+
+// floats per partial slot: O [mt][512], m [mt], l [mt]
+__host__ __device__ constexpr long long slot_floats(int mt) { return (long long)mt * (DV + 2); }
+
+struct Geom {
+  int q0, Q, kv0, N, P, R, T, NB;
+};
+
+__device__ inline Geom geom(const int32_t* qo, const int32_t* kvp, int r, int H, int mt) {
+  Geom g;
+  g.q0 = qo[r];
+  g.Q = qo[r + 1] - g.q0;
+  g.kv0 = kvp[r];
+  g.N = kvp[r + 1] - g.kv0;
+  g.P = g.N - g.Q;
+  if (g.Q < 1 || g.P < 0) {
+    g.R = g.T = g.NB = 0;
+  } else {
+    g.R = g.Q * H;
+    g.T = (g.R + mt - 1) / mt;
+    g.NB = (g.N + KB - 1) / KB;
+  }
+  return g;
+}
+
+__device__ inline long long units_of(const Geom& g) { return (long long)g.T * g.NB; }
+
+__device__ inline long long shfl_ll(long long v, int src) {
+  int lo = __shfl((int)(v & 0xffffffffLL), src);
+  int hi = __shfl((int)(v >> 32), src);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
+__device__ inline long long shfl_up_ll(long long v, int d) {
+  int lo = __shfl_up((int)(v & 0xffffffffLL), d);
+  int hi = __shfl_up((int)(v >> 32), d);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
+// Wave-cooperative (all 64 lanes call it): units of requests [0, rmax).
+__device__ inline long long units_before(int rmax, const int32_t* qo, const int32_t* kvp, int H,
+                                         int mt) {
+  const int lane = threadIdx.x & 63;
+  long long tot = 0;
+  for (int r0 = 0; r0 < rmax; r0 += 64) {
+    const int r = r0 + lane;
+    long long u = r < rmax ? units_of(geom(qo, kvp, r, H, mt)) : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      int lo = __shfl_xor((int)(u & 0xffffffffLL), off);
+      int hi = __shfl_xor((int)(u >> 32), off);
+      u += ((long long)hi << 32) | (unsigned int)lo;
+    }
+    tot += u;
+  }
+  return tot;
+}
+
+// Wave-cooperative: request r whose unit range [start, start + units) holds
+// unit u (r = bs if u is past the end).
+__device__ inline void locate(long long u, const int32_t* qo, const int32_t* kvp, int bs, int H,
+                              int mt, int& r_out, long long& start_out) {
+  const int lane = threadIdx.x & 63;
+  long long base = 0;
+  for (int r0 = 0; r0 < bs; r0 += 64) {
+    const int r = r0 + lane;
+    const long long ur = r < bs ? units_of(geom(qo, kvp, r, H, mt)) : 0;
+    long long incl = ur;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      long long v = shfl_up_ll(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const long long chunk = shfl_ll(incl, 63);
+    if (u < base + chunk) {
+      const unsigned long long m = __ballot(base + incl > u);
+      const int f = __ffsll((long long)m) - 1;
+      r_out = r0 + f;
+      start_out = base + shfl_ll(incl, f) - shfl_ll(ur, f);
+      return;
+    }
+    base += chunk;
+  }
+  r_out = bs;
+  start_out = base;
+}
+
+__device__ inline int effective_groups(long long U, int G) {
+  long long g = U / MIN_UNITS;
+  if (g < 1) g = 1;
+  return (int)(g < G ? g : G);
+}
+
+// first unit of workgroup w under the persistent schedule
+__device__ inline long long range_begin(long long w, long long U, long long Ge) { return w * U / Ge; }
+
+// workgroup whose persistent range holds unit u
+__device__ inline long long group_of(long long u, long long U, long long Ge) {
+  return ((u + 1) * Ge + U - 1) / U - 1;
+}
+
+}  // namespace attn
+}  // namespace ddtree
+
+// Launchers (defined in verify_attn.hip / verify_attn_bf16.hip)
+namespace ddtree {
+namespace attn {
+int launch_f32(const Params& p, int grid, hipStream_t s);
+int launch_bf16(const Params& p, int grid, hipStream_t s);
+int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s);
+}  // namespace attn
+}  // namespace ddtree

@@ -1,0 +1,280 @@
+// ddtree_verify_attn: host entry, the fp32 kernel and the partial merge.
+//
+// Attention of every (tree node, head) row over its request's prefix columns
+// plus the columns of its own ancestors, in absorbed-MLA form: the score is
+// the 576-wide dot product of the absorbed query with a latent row, the
+// output the softmax-weighted sum of the rows' first 512 (c_kv) entries ("The
+// Architecture of a Speculative Decoding Engine ...", section "The Forward
+// Pass Pseudocode"; "The 30-Column Mask ...", sections "The Message: Tensor
+// Shapes as Evidence" and "The Fix: Building Combined Indices").
+//
+// Softmax runs in base 2 on scores pre-multiplied by scale*log2(e); partial
+// results keep (unnormalised O, running max m, running sum l) and merge as
+//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  O = sum_s O_s 2^(m_s - M) / L,
+//   lse = ln 2 * (M + log2 L).
+#include <cmath>
+
+#include "attn_common.h"
+#include "common.h"
+
+namespace ddtree {
+namespace attn {
+
+namespace {
+
+constexpr float LN2 = 0.693147180559945309f;
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// fp32 path: one wavefront per query row, columns one at a time.  Lane k
+// owns latent entries k + 64j (9 of the 576 for the score, 8 of the 512
+// for the output).
+__global__ __launch_bounds__(256) void attn_f32_kernel(Params p) {
+  const int S = p.S;
+  const int wg = blockIdx.x;
+  const int s = wg % S;
+  const int t = (wg / S) % p.T_max;
+  const int r = wg / (S * p.T_max);
+  if (r >= p.bs) return;
+  const Geom g = geom(p.qo, p.kvp, r, p.H, MT_F32);
+  if (t >= g.T) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rho = t * MT_F32 + wave;
+  if (rho >= g.R) return;  // this kernel has no barriers
+  const int i = rho / p.H;
+  const float* qrow = static_cast<const float*>(p.q) + ((size_t)g.q0 * p.H + rho) * LATENT;
+  float qv[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) qv[k] = qrow[lane + 64 * k];
+  const int b0 = (int)((long long)s * g.NB / S);
+  const int b1 = (int)((long long)(s + 1) * g.NB / S);
+  const int c0 = b0 * KB, c1 = min(b1 * KB, g.N);
+  const uint32_t* vrow = p.vis + (size_t)(g.q0 + i) * p.W;
+  const float* pool = static_cast<const float*>(p.pool);
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = 0.f;
+  for (int c = c0; c < c1; ++c) {
+    if (c >= g.P) {
+      const int j = c - g.P;
+      if ((j >> 5) >= p.W || !((vrow[j >> 5] >> (j & 31)) & 1u)) continue;
+    }
+    long long slot = p.kvi[g.kv0 + c];
+    slot = slot < 0 ? 0 : (slot >= p.num_slots ? p.num_slots - 1 : slot);
+    const float* kv = pool + slot * LATENT;
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) d = fmaf(qv[k], kv[lane + 64 * k], d);
+    const float sv = wave_sum(d) * p.scale_log2;
+    const float mn = fmaxf(m, sv);
+    const float alpha = exp2f(m - mn);
+    const float pw = exp2f(sv - mn);
+    l = l * alpha + pw;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = fmaf(pw, kv[lane + 64 * k], o[k] * alpha);
+    m = mn;
+  }
+  const size_t orow = (size_t)g.q0 * p.H + rho;
+  if (S == 1) {
+    float* out = static_cast<float*>(p.out) + orow * DV;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[lane + 64 * k] = o[k] * inv;
+    if (lane == 0 && p.lse) p.lse[orow] = (m + log2f(l)) * LN2;
+  } else {
+    float* base = p.ws + (((long long)r * p.T_max + t) * S + s) * slot_floats(MT_F32);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) base[wave * DV + lane + 64 * k] = o[k];
+    if (lane == 0) {
+      base[MT_F32 * DV + wave] = m;
+      base[MT_F32 * DV + MT_F32 + wave] = l;
+    }
+  }
+}
+
+// One workgroup per row tile: combine the tile's partial slots.
+__global__ __launch_bounds__(256) void merge_kernel(Params p, int mt, int G, int dtype) {
+  const int tile = blockIdx.x;
+  const int r = tile / p.T_max, t = tile % p.T_max;
+  if (r >= p.bs) return;
+  const Geom g = geom(p.qo, p.kvp, r, p.H, mt);
+  if (t >= g.T) return;
+  long long first_slot = 0, w_first = 0, tile_start = 0, U = 0, Ge = 1;
+  int nseg;
+  if (p.S > 0) {
+    nseg = p.S;
+    first_slot = ((long long)r * p.T_max + t) * p.S;
+  } else {
+    U = units_before(p.bs, p.qo, p.kvp, p.H, mt);
+    if (U <= 0) return;
+    Ge = effective_groups(U, G);
+    tile_start = units_before(r, p.qo, p.kvp, p.H, mt) + (long long)t * g.NB;
+    w_first = group_of(tile_start, U, Ge);
+    const long long w_last = group_of(tile_start + g.NB - 1, U, Ge);
+    if (w_first == w_last) return;  // one workgroup covered the tile and wrote it
+    nseg = (int)(w_last - w_first + 1);
+  }
+  const int rows = min(mt, g.R - t * mt);
+  const long long sf = slot_floats(mt);
+  for (int idx = threadIdx.x; idx < rows * (DV / 4); idx += blockDim.x) {
+    const int row = idx / (DV / 4);
+    const int f4 = (idx % (DV / 4)) * 4;
+    float M = -INFINITY;
+    for (int k = 0; k < nseg; ++k) {
+      long long slot;
+      if (p.S > 0) {
+        slot = first_slot + k;
+      } else {
+        const long long w = w_first + k;
+        slot = 2 * w + (range_begin(w, U, Ge) >= tile_start ? 0 : 1);
+      }
+      M = fmaxf(M, p.ws[slot * sf + (long long)mt * DV + row]);
+    }
+    float L = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int k = 0; k < nseg; ++k) {
+      long long slot;
+      if (p.S > 0) {
+        slot = first_slot + k;
+      } else {
+        const long long w = w_first + k;
+        slot = 2 * w + (range_begin(w, U, Ge) >= tile_start ? 0 : 1);
+      }
+      const float* base = p.ws + slot * sf;
+      const float ms = base[(long long)mt * DV + row];
+      const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      L = fmaf(wgt, base[(long long)mt * DV + mt + row], L);
+      const float4 ov = *reinterpret_cast<const float4*>(base + (long long)row * DV + f4);
+      a0 = fmaf(wgt, ov.x, a0);
+      a1 = fmaf(wgt, ov.y, a1);
+      a2 = fmaf(wgt, ov.z, a2);
+      a3 = fmaf(wgt, ov.w, a3);
+    }
+    const float inv = 1.f / L;
+    const size_t orow = (size_t)g.q0 * p.H + (size_t)t * mt + row;
+    if (dtype == DDTREE_BF16) {
+      __bf16* out = static_cast<__bf16*>(p.out) + orow * DV + f4;
+      out[0] = (__bf16)(a0 * inv);
+      out[1] = (__bf16)(a1 * inv);
+      out[2] = (__bf16)(a2 * inv);
+      out[3] = (__bf16)(a3 * inv);
+    } else {
+      float* out = static_cast<float*>(p.out) + orow * DV + f4;
+      out[0] = a0 * inv;
+      out[1] = a1 * inv;
+      out[2] = a2 * inv;
+      out[3] = a3 * inv;
+    }
+    if (f4 == 0 && p.lse) p.lse[orow] = (M + log2f(L)) * LN2;
+  }
+}
+
+}  // namespace
+
+int launch_f32(const Params& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(grid), dim3(256), 0, s, p);
+  return check_launch("verify_attn(f32)");
+}
+
+int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s) {
+  const long long tiles = (long long)p.bs * p.T_max;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)tiles), dim3(256), 0, s, p, mt, grid_groups,
+                     dtype);
+  return check_launch("verify_attn(merge)");
+}
+
+static int bf16_grid() { return device_cu_count(); }
+
+}  // namespace attn
+}  // namespace ddtree
+
+using namespace ddtree::attn;
+
+extern "C" size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int max_q_len,
+                                                    int max_kv_len, int num_splits, int dtype) {
+  if (bs <= 0 || num_heads < 1 || max_q_len < 1 || max_kv_len < max_q_len || num_splits < 0)
+    return 0;
+  if (dtype != DDTREE_F32 && dtype != DDTREE_BF16) return 0;
+  const int mt = dtype == DDTREE_BF16 ? MT_BF16 : MT_F32;
+  const long long T_max = ((long long)max_q_len * num_heads + mt - 1) / mt;
+  long long slots = 0;
+  if (num_splits == 0) {
+    if (dtype == DDTREE_BF16) slots = 2LL * bf16_grid();
+  } else if (num_splits > 1) {
+    slots = (long long)bs * T_max * num_splits;
+  }
+  return (size_t)(slots * slot_floats(mt) * (long long)sizeof(float));
+}
+
+extern "C" int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t num_slots,
+                                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* qo_indptr, const uint32_t* vis_bits,
+                                  int words_per_row, int bs, int num_heads, int max_q_len,
+                                  int max_kv_len, float scale, int dtype, void* out, float* lse,
+                                  int num_splits, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  ddtree::clear_error();
+  DDTREE_REQUIRE(bs >= 0, DDTREE_EINVAL, "verify_attn: bs must be >= 0");
+  if (bs == 0) return DDTREE_OK;
+  DDTREE_REQUIRE(q && kv_pool && kv_indptr && kv_indices && qo_indptr && vis_bits && out,
+                 DDTREE_EINVAL, "verify_attn: null required pointer");
+  DDTREE_REQUIRE(num_heads >= 1, DDTREE_EINVAL, "verify_attn: num_heads must be >= 1");
+  DDTREE_REQUIRE(max_q_len >= 1, DDTREE_EINVAL, "verify_attn: max_q_len must be >= 1");
+  DDTREE_REQUIRE(max_kv_len >= max_q_len, DDTREE_EINVAL,
+                 "verify_attn: max_kv_len (%d) < max_q_len (%d)", max_kv_len, max_q_len);
+  DDTREE_REQUIRE((long long)words_per_row * 32 >= max_q_len, DDTREE_EINVAL,
+                 "verify_attn: words_per_row %d too small for max_q_len %d", words_per_row,
+                 max_q_len);
+  DDTREE_REQUIRE(std::isfinite(scale), DDTREE_EINVAL, "verify_attn: scale must be finite");
+  DDTREE_REQUIRE(num_slots >= 1, DDTREE_EINVAL, "verify_attn: num_slots must be >= 1");
+  DDTREE_REQUIRE(num_splits >= 0, DDTREE_EINVAL, "verify_attn: num_splits must be >= 0");
+  DDTREE_REQUIRE(dtype == DDTREE_F32 || dtype == DDTREE_BF16, DDTREE_EINVAL,
+                 "verify_attn: unknown dtype %d", dtype);
+  const size_t need = ddtree_verify_attn_workspace_size(bs, num_heads, max_q_len, max_kv_len,
+                                                        num_splits, dtype);
+  DDTREE_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), DDTREE_EWORKSPACE,
+                 "verify_attn: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  const int mt = dtype == DDTREE_BF16 ? MT_BF16 : MT_F32;
+  const long long T_max = ((long long)max_q_len * num_heads + mt - 1) / mt;
+  DDTREE_REQUIRE(T_max * bs * (num_splits > 0 ? num_splits : 1) < (1LL << 31), DDTREE_EUNSUPPORTED,
+                 "verify_attn: grid too large");
+
+  Params p;
+  p.q = q;
+  p.pool = kv_pool;
+  p.num_slots = num_slots;
+  p.kvp = kv_indptr;
+  p.kvi = kv_indices;
+  p.qo = qo_indptr;
+  p.vis = vis_bits;
+  p.W = words_per_row;
+  p.bs = bs;
+  p.H = num_heads;
+  p.T_max = (int)T_max;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.out = out;
+  p.lse = lse;
+  p.ws = static_cast<float*>(workspace);
+  hipStream_t s = ddtree::as_stream(stream);
+
+  if (dtype == DDTREE_F32) {
+    p.S = num_splits == 0 ? 1 : num_splits;
+    int rc = launch_f32(p, (int)(bs * T_max * p.S), s);
+    if (rc != DDTREE_OK || p.S == 1) return rc;
+    return launch_merge(p, mt, 0, dtype, s);
+  }
+  p.S = num_splits;
+  int G;
+  if (num_splits == 0) {
+    G = bf16_grid();
+    DDTREE_REQUIRE(G > 0, DDTREE_EHIP, "verify_attn: cannot query the device compute units");
+  } else {
+    G = (int)(bs * T_max * num_splits);
+  }
+  int rc = launch_bf16(p, G, s);
+  if (rc != DDTREE_OK || num_splits == 1) return rc;
+  return launch_merge(p, mt, G, dtype, s);
+}

@@ -1,0 +1,109 @@
+"""One DDTree verify step on device tensors: build -> visibility -> attention -> accept.
+
+``VerifyStep`` owns the output and workspace tensors (torch allocations, made
+once) and enqueues the four library calls on the current stream with no host
+synchronisation, so a step can be timed with events or captured in a graph.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+LATENT = 576
+DV = 512
+
+
+@dataclass
+class StepInputs:
+    """Device tensors and host-known sizes of one batch (request order = index order)."""
+    topk_logprobs: torch.Tensor   # [bs, D, K] f32
+    topk_ids: torch.Tensor        # [bs, D, K] i32
+    root_tokens: torch.Tensor     # [bs] i32
+    qo_indptr: torch.Tensor       # [bs+1] i32
+    kv_indptr: torch.Tensor       # [bs+1] i32
+    kv_indices: torch.Tensor      # [sum(P_r+Q_r)] i32
+    prefix_lens: torch.Tensor     # [bs] i32
+    q: torch.Tensor               # [total_q, H, 576] bf16 | f32
+    kv_pool: torch.Tensor         # [num_slots, 576] bf16 | f32
+    total_q: int
+    max_q_len: int
+    max_kv_len: int
+    max_budget: int
+    scale: float
+    target_predict: Optional[torch.Tensor] = None  # [total_q] i32
+
+    @property
+    def bs(self) -> int:
+        return self.qo_indptr.numel() - 1
+
+    @property
+    def heads(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def depth(self) -> int:
+        return self.topk_logprobs.shape[1]
+
+
+class VerifyStep:
+    def __init__(self, x: StepInputs, num_splits: int = 0, want_lse: bool = True,
+                 want_positions: bool = True):
+        dev = x.q.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.x = x
+        self.num_splits = int(num_splits)
+        self.words = (x.max_q_len + 31) // 32
+        self.node_tokens = torch.empty(x.total_q, **i32)
+        self.node_parents = torch.empty(x.total_q, **i32)
+        self.node_depths = torch.empty(x.total_q, **i32)
+        self.node_scores = torch.empty(x.total_q, dtype=torch.float32, device=dev)
+        self.vis_bits = torch.empty(x.total_q, self.words, **i32)
+        self.positions = torch.empty(x.total_q, dtype=torch.int64, device=dev) if want_positions else None
+        self.out = torch.empty(x.total_q, x.heads, DV, dtype=x.q.dtype, device=dev)
+        self.lse = torch.empty(x.total_q, x.heads, dtype=torch.float32, device=dev) if want_lse else None
+        dt = _lib.DDTREE_BF16 if x.q.dtype == torch.bfloat16 else _lib.DDTREE_F32
+        ws = _lib.ddtree_verify_attn_workspace_size(x.bs, x.heads, x.max_q_len, x.max_kv_len,
+                                                    self.num_splits, dt)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        D = x.depth
+        self.accepted_nodes = torch.empty(x.bs, D + 1, **i32)
+        self.accept_len = torch.empty(x.bs, **i32)
+        self.commit_tokens = torch.empty(x.bs, D + 1, **i32)
+        self.bonus_tokens = torch.empty(x.bs, **i32)
+
+    def build(self, stream=None):
+        x = self.x
+        _lib.ddtree_build_tree(x.topk_logprobs, x.topk_ids, x.root_tokens, x.qo_indptr,
+                               x.max_budget, self.node_tokens, self.node_parents,
+                               self.node_depths, self.node_scores, stream=stream)
+
+    def visibility(self, stream=None):
+        x = self.x
+        _lib.ddtree_compile_visibility(self.node_parents, self.node_depths, x.qo_indptr,
+                                       x.prefix_lens, x.max_q_len, self.vis_bits,
+                                       positions=self.positions, stream=stream)
+
+    def attention(self, stream=None):
+        x = self.x
+        _lib.ddtree_verify_attn(x.q, x.kv_pool, x.kv_indptr, x.kv_indices, x.qo_indptr,
+                                self.vis_bits, x.max_q_len, x.max_kv_len, x.scale, self.out,
+                                lse=self.lse, num_splits=self.num_splits,
+                                workspace=self.workspace, stream=stream)
+
+    def accept(self, target_predict=None, stream=None):
+        x = self.x
+        tp = x.target_predict if target_predict is None else target_predict
+        _lib.ddtree_accept(self.node_tokens, self.node_parents, x.qo_indptr, tp, x.depth,
+                           self.accepted_nodes, self.accept_len, self.commit_tokens,
+                           self.bonus_tokens, stream=stream)
+
+    def run(self, stream=None):
+        """All four stages (accept needs ``target_predict`` in the inputs)."""
+        self.build(stream)
+        self.visibility(stream)
+        self.attention(stream)
+        self.accept(stream=stream)
