@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of one DDTree verify step on one MI355X.
+
+A step = build the draft trees -> compile visibility (bitsets + positions)
+-> tree-verify attention -> greedy accept, over one batch of the workload
+"64 heads, 33-node trees, 8k context": bs 8, 64 heads, budget 32 (q_len
+33), prefix 8192 per request, bf16 latents in a 300k-slot pool, top-8
+per-depth log-probs, seeded synthetic inputs.
+
+Timing: W untimed warm-up steps, then exactly K steps between two
+synchronisations, bracketed by HIP events on the stream every stage is
+launched on.  Steps rotate over R independent instances (separate pools) so
+more than 512 MB is touched between two uses of one instance, i.e. the
+numbers are not served from the 256 MB last-level cache.
+
+Prints one JSON line.  ``value`` = algorithmic attention TFLOP/s of the whole
+step (attention flops / step time); ``roofline`` = the verify-attention call
+(matrix-core kernel + partial merge) against the bf16 MFMA peak;
+``cpu_baseline`` = the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+FLOP_PER_PAIR = 2 * 576 + 2 * 512  # score dot product + value accumulation per (row, column)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default: the headline, 3)")
+    ap.add_argument("--instances", type=int, default=8, help="rotated independent instances")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_work(wl, depths):
+    """(attention flops, attention bytes) the method itself needs for this batch."""
+    H = wl.heads
+    flops = 0
+    nbytes = 0
+    elt = 2 if wl.dtype == "bf16" else 4
+    W = (wl.max_q_len + 31) // 32
+    for r in range(wl.bs):
+        a, b = int(wl.qo_indptr[r]), int(wl.qo_indptr[r + 1])
+        P = int(wl.prefix_lens[r])
+        Q = b - a
+        visible = Q * P + int((np.asarray(depths[a:b]) + 1).sum())
+        flops += FLOP_PER_PAIR * H * visible
+        nbytes += (P + Q) * 576 * elt + (P + Q) * 4          # latent rows once + slot indices
+        nbytes += Q * H * (576 + 512) * elt + Q * H * 4      # q in, out + lse
+        nbytes += Q * W * 4                                   # ancestor bitsets
+    return flops, nbytes
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The CPU oracle as it stands, on whole requests of the workload until the budget is used."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import accept, attention, tree, visibility
+    from workloads import draw_target_predict
+
+    done, flops, t0 = 0, 0, time.perf_counter()
+    for r in range(wl.bs):
+        a, b = int(wl.qo_indptr[r]), int(wl.qo_indptr[r + 1])
+        t = tree.build_tree(wl.topk_logprobs[r], wl.topk_ids[r], int(wl.root_tokens[r]), b - a - 1)
+        P = int(wl.prefix_lens[r])
+        visibility.vis_bits(t.parents, (wl.max_q_len + 31) // 32)
+        visibility.positions(t.depths, P)
+        attention.verify_request(wl.q_f32()[a:b], wl.kv_rows_f32(wl.request_slots(r)), P,
+                                 t.parents, float(np.float32(wl.scale)))
+        pred = draw_target_predict(wl.seed, t.tokens, t.parents, np.array([0, b - a]), wl.vocab)
+        accept.accept(t.tokens, t.parents, pred, wl.depth)
+        flops += FLOP_PER_PAIR * wl.heads * ((b - a) * P + int((t.depths + 1).sum()))
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {wl.bs} requests (tree + visibility + fp64 attention + accept), "
+                      f"{dt:.1f} s wall, {len(os.sched_getaffinity(0))} host cores visible",
+            "tree_steps_per_s": done / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verify path is built and timed on a single MI355X; "
+              "run it with --gpus 1 (multi-GPU sharding is described in DESIGN.md, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tree_verify_mla_amd.step import VerifyStep
+    from workloads import draw_target_predict, get_config, make_workload
+    from workloads.device import to_device
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+
+    # ---- instances (rotated so the timed steps do not run out of cache) ----
+    R = max(1, args.instances)
+    wls, steps = [], []
+    for k in range(R):
+        wl = make_workload(cfg, seed=cfg.seed + 1000 * k, unused="zero")
+        x = to_device(wl, "cuda")
+        st = VerifyStep(x, num_splits=args.num_splits)
+        st.build()
+        torch.cuda.synchronize()
+        tok = st.node_tokens.cpu().numpy()
+        par = st.node_parents.cpu().numpy()
+        x.target_predict = torch.from_numpy(
+            draw_target_predict(wl.seed, tok, par, wl.qo_indptr, wl.vocab)).cuda()
+        wls.append(wl)
+        steps.append(st)
+        print(f"instance {k}: {wl.name} bs={wl.bs} H={wl.heads} total_q={wl.total_q} "
+              f"max_kv={wl.max_kv_len}", file=sys.stderr, flush=True)
+    depths = steps[0].node_depths.cpu().numpy()
+    flops, nbytes = algorithmic_work(wls[0], depths)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        steps[i % R].run(stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        st = steps[i % R]
+        e = ev[i]
+        e[0].record(stream)
+        st.build(stream)
+        st.visibility(stream)
+        e[1].record(stream)
+        st.attention(stream)
+        e[2].record(stream)
+        st.accept(stream=stream)
+        e[3].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / K
+    tv_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    acc_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    value = flops / (step_ms * 1e-3) / 1e12
+    gbps = nbytes / (attn_ms * 1e-3) / 1e9
+    line = {
+        "metric": "verify-attn TFLOP/s + % of MFMA/HBM roofline, 33-node tree, 64 heads, 8k ctx",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wls[0].dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random latents, drafter top-k from N(0,1) logits)",
+        "config": {"workload": wls[0].name, "bs": wls[0].bs, "heads": wls[0].heads,
+                   "q_len": int(wls[0].max_q_len), "prefix": int(wls[0].prefix_lens.max()),
+                   "topk": wls[0].topk, "pool_slots": wls[0].num_slots, "instances": R,
+                   "num_splits": args.num_splits, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "ddtree_verify_attn (attn_bf16_kernel + merge_kernel)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
+        "extra": {"attn_ms": round(attn_ms, 5), "build_visibility_ms": round(tv_ms, 5),
+                  "accept_ms": round(acc_ms, 5),
+                  "attn_GBps": round(gbps, 1), "attn_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                  "tree_steps_per_s": round(wls[0].bs / (step_ms * 1e-3), 1)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wls[0], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
