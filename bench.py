@@ -46,7 +46,22 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run 5 device-to-device copies of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    """Plain copies of known size: FETCH_SIZE / WRITE_SIZE of these dispatches
+    give the factor that turns the counters into bytes."""
+    import torch
+
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": mib << 20, "copies": 5}), flush=True)
 
 
 def algorithmic_work(wl, depths):
@@ -108,6 +123,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+        return
 
     from tree_verify_mla_amd.step import VerifyStep
     from workloads import draw_target_predict, get_config, make_workload

@@ -39,12 +39,8 @@ DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ff
 
 def _compile(src: Path, verbose: bool) -> Path:
     obj = BUILD / (src.name + ".o")
-    cmd = [hipcc(), *COMMON, "-c", str(src), "-o", str(obj)]
-    if src.suffix == ".hip":
-        cmd[1:1] = ["-x", "hip"]
-        cmd += DEVICE_ONLY
-    else:
-        cmd += ["-x", "c++"]
+    # every source (the .cpp host files too) goes through the HIP language mode
+    cmd = [hipcc(), "-x", "hip", *COMMON, "-c", str(src), "-o", str(obj), *DEVICE_ONLY]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

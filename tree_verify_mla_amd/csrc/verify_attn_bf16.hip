@@ -27,18 +27,27 @@
 // Splitting the pair this way keeps each LDS byte feeding 32 rows while a
 // wave needs only 72 VGPRs of queries and 128 accumulators of output.
 //
-// LDS: two 36 KB buffers (32 latent rows of 1152 B) plus a ring of three
-// 32-entry slot-index lists.  Block b+1 streams in with
-// global_load_lds_dwordx4 (global -> LDS, no registers) while block b is
-// computed; its slot indices were fetched the same way one block earlier, so
-// the gather never waits on an index load.
-//
+// Block buffer layout.  A block is 32 latent rows x 72 chunks of 16 bytes.
+// The buffer is 36 groups of 1 KB; group j holds chunks 2j and 2j+1 of all
+// 32 rows, chunk 2j+q of row r at 16-byte position
+//   pos(r, q, j) = 16 * ((r >> 4) + 2q) + ((r + 4q + 8 * (j & 1)) & 15).
+// * gather: one global_load_lds_dwordx4 fills one group (lane = position);
+//   the waves of one parity of j see the same (row, q) per lane, so a lane
+//   computes one pool address per block and adds 32 * j per load.
+// * score fragment (k-step j, lane l: row l & 31, chunk 2j + (l >> 5)): two
+//   base addresses (j even / odd) plus an immediate 1 KB * j.
+// * transposed value fragments (4 rows x 16 features per 16 lanes): two
+//   base addresses plus immediates.
 // gfx950 LDS has 64 four-byte banks; a b128 read is serviced 16 lanes at a
-// time, a b64 (and the transposing b64) read 32 lanes at a time.  Row r's
-// 16-byte chunks are XOR-swizzled inside each 128-byte group,
-//   chunk' = chunk ^ h(r),  h(r) = ((r >> 1) & 1) << 2 | ((r >> 2) & 3),
-// which makes both access patterns conflict-free: the K reads (16 rows, one
-// chunk each) and the transposed V reads (4 rows x 4 adjacent chunks).
+// time, a b64 (and the transposing b64) read 32 lanes at a time.  In both
+// patterns the lanes of one phase land on 16 distinct positions mod 16, so
+// neither has bank conflicts.
+//
+// Pipeline: four block buffers, two blocks in flight.  Iteration b holds the
+// partial scores of block b; it starts the gather of block b+3, completes
+// S(b) with the partner's half and runs its softmax under the 18 score
+// MFMAs of block b+1, then runs the 16 value MFMAs of block b with the rest
+// of the exponentials underneath and hands S(b+1)'s half to the partner.
 #include "attn_common.h"
 #include "common.h"
 
@@ -56,31 +65,74 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int ROWB = LATENT * 2;   // 1152 bytes per latent row
 constexpr int BUFB = KB * ROWB;    // 36864 bytes per block buffer
-constexpr int LOADS = BUFB / 1024; // 36 global_load_lds_dwordx4 (64 lanes x 16 B) per block
-constexpr int RING_SLOT = 64 * 4;  // bytes per slot-index list (64 lanes x int32)
+constexpr int LOADS = BUFB / 1024; // 36 one-KB groups per block
+constexpr int NBUF = 4;            // block buffers: two blocks in flight
 constexpr int XCH = 64 * 64;       // bytes per wave of score-exchange space (64 lanes x 16 f32)
 constexpr int KS_HALF = 18;        // k-steps of 16 features per half of the 576-wide score
 constexpr int FB_HALF = 8;         // 32-feature output blocks per half of the 512 outputs
 constexpr float LN2 = 0.693147180559945309f;
 
-__device__ inline int swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14)
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
+constexpr int WAIT_LGKM0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
 
-__device__ inline bf16x8_t lds_read_b128(const lds_char* base, int off) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(base + off);
+__device__ inline int chunk_pos(int r, int q, int jodd) {
+  return 16 * ((r >> 4) + 2 * q) + ((r + 4 * q + 8 * jodd) & 15);
 }
 
-__device__ inline bf16x4_t lds_read_tr(const lds_char* base, int off) {
+// Workgroup barrier that waits only for this wave's LDS traffic, leaving the
+// global->LDS gathers of later blocks in flight (__syncthreads() would wait
+// for every outstanding memory operation).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// The gather and its slot-index loads are issued as inline asm so that the
+// compiler's wait-count model does not see them: it cannot tell the
+// global->LDS writes from the transposing LDS reads of other buffers and
+// would otherwise wait for every gather in flight before each of those
+// reads.  Ordering is explicit instead: every consumer of a gathered block
+// or of a loaded index sits behind an s_waitcnt vmcnt that retires it.
+// The "memory" clobber keeps all other memory accesses on their side.
+__device__ inline void gather16(const char* src, const lds_char* dst) {
+  // 16 bytes per lane: LDS address = M0 + 16 * lane
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"((unsigned)(size_t)dst)
+               : "memory");
+}
+__device__ inline int load_async(const int32_t* ptr) {
+  // the result may be read only after an s_waitcnt that retires this load
+  int v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(ptr) : "memory");
+  return v;
+}
+
+__device__ inline long long uni64(long long x) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(x & 0xffffffffLL));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
+// Every lane computed the same request geometry from the same loads; saying
+// so lets the compiler keep it in scalar registers and branch on it.
+__device__ inline Geom uniform(Geom g) {
+  g.q0 = uni(g.q0); g.Q = uni(g.Q); g.kv0 = uni(g.kv0); g.N = uni(g.N);
+  g.P = uni(g.P); g.R = uni(g.R); g.T = uni(g.T); g.NB = uni(g.NB);
+  return g;
+}
+
+__device__ inline bf16x8_t lds_read_b128(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(p);
+}
+
+__device__ inline bf16x4_t lds_read_tr(const lds_char* p) {
   i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(
-          const_cast<lds_char*>(base + off)));
+      reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(const_cast<lds_char*>(p)));
   return __builtin_bit_cast(bf16x4_t, v);
-}
-
-__device__ inline float max16(const f32x16_t& v) {
-  float m = v[0];
-#pragma unroll
-  for (int k = 1; k < 16; ++k) m = fmaxf(m, v[k]);
-  return m;
 }
 
 __device__ inline float other_half(float x) {
@@ -93,82 +145,115 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
   constexpr int MT = 16 * NW;
   static_assert(MT == MT_BF16, "tile rows must match the schedule");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUFB + NW * XCH + 3 * RING_SLOT];
+  static_assert(NW % 2 == 0 && LOADS % NW == 0, "gather groups must split evenly by parity");
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUFB + NW * XCH];
   lds_char* lds = (lds_char*)smem;  // generic -> LDS address space
-  lds_char* xch = lds + 2 * BUFB;
-  lds_char* ring = xch + NW * XCH;
+  lds_char* xch = lds + NBUF * BUFB;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int pair = wave >> 1, half = wave & 1;
   const __bf16* __restrict__ qg = static_cast<const __bf16*>(p.q);
-  const __bf16* __restrict__ pool = static_cast<const __bf16*>(p.pool);
+  const char* __restrict__ poolb = static_cast<const char*>(p.pool);
+  const int xmine = wave * XCH + lane * 16;
+  const int xpart = (wave ^ 1) * XCH + lane * 16;
 
-  // ---- per-lane LDS offsets (layouts in the header comment) ----
-  // K fragment of k-step ks: row l32, logical chunk 2*ks + hl.
-  const int kbase = l32 * ROWB;
-  int kin[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) kin[e] = 16 * ((2 * e + hl) ^ swz(l32));
-  // V^T fragment via ds_read_b64_tr_b16: in each 16-lane group, lane c
-  // supplies row (c / 4) and 4 features at 4 * (c % 4) of a 4 x 16 block.
-  const int c16 = lane & 15, G = lane >> 4;
-  const int vbase = (4 * hl + (c16 >> 2)) * ROWB + 8 * (c16 & 1);
-  const int e0 = 2 * (G & 1) + ((c16 & 3) >> 1);
-  const int hv0 = (((c16 >> 3) & 1) << 2) | (hl & 3);
-  const int hv1 = (((c16 >> 3) & 1) << 2) | ((2 + hl) & 3);
-  const int vin00 = 16 * (e0 ^ hv0), vin01 = 16 * ((4 + e0) ^ hv0);
-  const int vin10 = 16 * (e0 ^ hv1), vin11 = 16 * ((4 + e0) ^ hv1);
-  // score exchange: chunk k (4 floats) of lane l at (k * 64 + l) * 16
-  lds_char* xmine = xch + wave * XCH + lane * 16;
-  const lds_char* xpart = xch + (wave ^ 1) * XCH + lane * 16;
+  // ---- lane constants of the buffer layout (header comment) ----
+  // score fragments: k-step 18 * half + k at kofs[k & 1] + 1024 * k
+  const int kofs0 = KS_HALF * 1024 * half + 16 * chunk_pos(l32, hl, 0);
+  const int kofs1 = KS_HALF * 1024 * half + 16 * chunk_pos(l32, hl, 1);
+  // value fragments of output block fb, column half k2, row quad t at
+  // vofs[t] + 2048 * fb + 256 * k2: 16-lane group g supplies block rows
+  // 16 k2 + 8 t + 4 (l >> 5) + (c >> 2) and features 16 (g & 1) + 4 (c & 3) .. +3
+  int vofs0, vofs1;
+  {
+    const int g16 = lane >> 4, cq = lane & 15, q = (cq & 3) >> 1;
+    const int x0 = (4 * hl + (cq >> 2) + 4 * q + 8 * (g16 & 1)) & 15;
+    const int vb = 16 * 1024 * half + 1024 * (g16 & 1) + 512 * q + 8 * (cq & 1);
+    vofs0 = vb + 16 * x0;
+    vofs1 = vb + 16 * (x0 ^ 8);
+  }
+  // gather: the block row and chunk parity this lane fetches (groups of parity `half`)
+  const int grow = 16 * ((lane >> 4) & 1) + (((lane & 15) - 4 * (lane >> 5) - 8 * half) & 15);
+  const int gq16 = 16 * (lane >> 5);
 
   // ---- schedule ----
-  long long U = 0, Ge = 1, u0 = 0, u1 = 0;
-  const int w = blockIdx.x;
+  // Persistent: G workgroups take equal contiguous ranges of the unit list.
+  // Workgroup w runs on XCD w % 8 (hardware round-robin), so ranges are
+  // handed out by "virtual" id v = (w % 8) * (G / 8) + w / 8: the 32
+  // workgroups of one XCD share a contiguous stretch of work -- for the
+  // 64-head batch exactly one request -- and re-read its KV blocks from that
+  // XCD's L2 instead of the last-level cache.
+  long long U = 0, Ge = 1, u0 = 0, u1 = 0, v = blockIdx.x;
   if (p.S == 0) {
-    U = units_before(p.bs, p.qo, p.kvp, p.H, MT);
+    U = uni64(units_before(p.bs, p.qo, p.kvp, p.H, MT));
     if (U <= 0) return;
     Ge = effective_groups(U, gridDim.x);
-    if (w >= Ge) return;
-    u0 = range_begin(w, U, Ge);
-    u1 = range_begin(w + 1, U, Ge);
+    if (blockIdx.x >= Ge) return;
+    if (Ge == gridDim.x && (Ge & 7) == 0) v = (blockIdx.x & 7) * (Ge >> 3) + (blockIdx.x >> 3);
+    u0 = range_begin(v, U, Ge);
+    u1 = range_begin(v + 1, U, Ge);
   }
 
-  long long u = u0;
-  bool first = true;
+  // A range is a run of segments, each inside one tile.  Only the first can
+  // start mid-tile; it runs last, so every workgroup sweeps its tiles' KV
+  // blocks from block 0 onward in step with the rest of its XCD.
+  long long cursor = 0;  // next unit among the segments after the first
+  bool first_done = false;
+  if (p.S == 0) {
+    int r0;
+    long long start0;
+    locate(u0, p.qo, p.kvp, p.bs, p.H, MT, r0, start0);
+    r0 = uni(r0);
+    if (r0 >= p.bs) return;
+    start0 = uni64(start0);
+    const Geom g0 = uniform(geom(p.qo, p.kvp, r0, p.H, MT));
+    cursor = start0 + min(((u0 - start0) / g0.NB + 1) * g0.NB, u1 - start0);
+  }
+  int seg_no = 0;
+  const int nslot_m1 = (int)min(p.num_slots - 1, (long long)0x7fffffff);
   while (true) {
     int r, t, b_begin, b_end;
     long long slot = -1;
     Geom g;
     if (p.S == 0) {
-      if (u >= u1) break;
+      long long useg;
+      if (cursor < u1) {
+        useg = cursor;
+      } else if (!first_done) {
+        useg = u0;
+        first_done = true;
+      } else {
+        break;
+      }
       long long start;
-      locate(u, p.qo, p.kvp, p.bs, p.H, MT, r, start);
+      locate(useg, p.qo, p.kvp, p.bs, p.H, MT, r, start);
+      r = uni(r);
       if (r >= p.bs) break;
-      g = geom(p.qo, p.kvp, r, p.H, MT);
-      const long long local = u - start;
-      t = (int)(local / g.NB);
-      b_begin = (int)(local % g.NB);
+      start = uni64(start);
+      g = uniform(geom(p.qo, p.kvp, r, p.H, MT));
+      const long long local = useg - start;
+      t = uni((int)(local / g.NB));
+      b_begin = uni((int)(local % g.NB));
       const long long seg_end = min((long long)(t + 1) * g.NB, u1 - start);
-      b_end = (int)(seg_end - (long long)t * g.NB);
-      if (!(b_begin == 0 && b_end == g.NB)) slot = 2LL * w + (first ? 0 : 1);
-      u = start + seg_end;
-      first = false;
+      b_end = uni((int)(seg_end - (long long)t * g.NB));
+      if (!(b_begin == 0 && b_end == g.NB)) slot = 2 * v + (useg == u0 ? 0 : 1);
+      if (useg != u0) cursor = start + seg_end;
     } else {
-      if (!first) break;
-      first = false;
+      if (seg_no > 0) break;
       const int S = p.S;
-      const int s = w % S;
-      t = (w / S) % p.T_max;
-      r = w / (S * p.T_max);
+      const int s = blockIdx.x % S;
+      t = (blockIdx.x / S) % p.T_max;
+      r = blockIdx.x / (S * p.T_max);
       if (r >= p.bs) break;
-      g = geom(p.qo, p.kvp, r, p.H, MT);
+      g = uniform(geom(p.qo, p.kvp, r, p.H, MT));
       if (t >= g.T) break;
-      b_begin = (int)((long long)s * g.NB / S);
-      b_end = (int)((long long)(s + 1) * g.NB / S);
+      b_begin = uni((int)((long long)s * g.NB / S));
+      b_end = uni((int)((long long)(s + 1) * g.NB / S));
       if (S > 1) slot = ((long long)r * p.T_max + t) * S + s;
     }
+    ++seg_no;
 
     // ---- this pair's 32 query rows; this wave's half of their features ----
     const int rho = t * MT + pair * 32 + l32;
@@ -181,177 +266,285 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
           qg + ((size_t)g.q0 * p.H + (row_ok ? rho : 0)) * LATENT + 8 * hl + 16 * KS_HALF * half;
 #pragma unroll
       for (int k = 0; k < KS_HALF; ++k) {
-        bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k);
-        if (!row_ok) v = bf16x8_t{};
-        qf[k] = v;
+        bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k);
+        if (!row_ok) x = bf16x8_t{};
+        qf[k] = x;
       }
     }
+    // The row's ancestor bitset words, read once per segment: a global load
+    // inside the block loop would have to wait behind the in-flight gathers.
+    // Rows of up to 128 tree nodes keep all words in registers.
     const uint32_t* vrow = p.vis + (size_t)(g.q0 + node) * p.W;
+    uint32_t vw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vw[k] = k < p.W ? vrow[k] : 0u;
 
     f32x16_t o[FB_HALF];
 #pragma unroll
     for (int fb = 0; fb < FB_HALF; ++fb) o[fb] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;
+    const float c = p.scale_log2;
 
-    // wave 0 fetches the slot indices of block b into ring slot b % 3
-    auto issue_idx = [&](int b) {
-      const int col = min(b * KB + lane, g.N - 1);
-      __builtin_amdgcn_global_load_lds(
-          p.kvi + g.kv0 + col,
-          reinterpret_cast<__attribute__((address_space(3))) void*>(ring + (b % 3) * RING_SLOT),
-          4, 0, 0);
-    };
-    // the waves share the 36 gathers (64 chunks of 16 B each) of block b
-    auto issue_data = [&](int b, int buf) {
-      const __attribute__((address_space(3))) int* idx =
-          reinterpret_cast<const __attribute__((address_space(3))) int*>(ring + (b % 3) * RING_SLOT);
+    // slot of the block row this lane gathers in block b (a register load,
+    // issued one block ahead of its use)
+    const int32_t* kvi = p.kvi + g.kv0;
+    auto load_idx = [&](int b) { return load_async(kvi + min(b * KB + grow, g.N - 1)); };
+    // this wave's share of the gather of block b: groups j = wave, wave + NW, ...
+    auto issue_data = [&](int b, int sid) {
+      sid = min(max(sid, 0), nslot_m1);
+      const char* src = poolb + (long long)sid * ROWB + gq16;
+      lds_char* dst = lds + (b % NBUF) * BUFB;
 #pragma unroll
-      for (int j = wave; j < LOADS; j += NW) {
-        const int pc = j * 64 + lane;  // physical 16-byte chunk of the buffer
-        const int row = pc / 72, c = pc % 72;
-        const int chunk = (c & ~7) | ((c & 7) ^ swz(row));
-        long long sid = idx[row];
-        sid = sid < 0 ? 0 : (sid >= p.num_slots ? p.num_slots - 1 : sid);
-        __builtin_amdgcn_global_load_lds(
-            pool + sid * LATENT + chunk * 8,
-            reinterpret_cast<__attribute__((address_space(3))) void*>(lds + buf * BUFB + j * 1024),
-            16, 0, 0);
+      for (int i = 0; i < LOADS / NW; ++i) {
+        const int j = wave + NW * i;
+        gather16(src + 32 * j, dst + 1024 * j);
       }
     };
+    constexpr int LPW = LOADS / NW;  // gather loads per wave per block
+    constexpr int KDEPTH = 4;        // score fragments read ahead (at most 4)
+    constexpr int VDEPTH = 2;        // value MFMAs whose fragments are read ahead
 
-    __syncthreads();  // the previous segment is done with the buffers and the ring
+    // ------------------------------------------------------------------
+    // Prologue: gather blocks b0 .. b0+2, compute this wave's half of S(b0),
+    // hand it to the partner, and read the first score fragments of b0+1.
+    // ------------------------------------------------------------------
+    __syncthreads();  // the previous segment is done with all buffers
+    f32x16_t s_mine = f32x16_t{};  // this wave's half of the scores of the current block
+    bf16x8_t kpre[KDEPTH];         // first score fragments of the next block
+#pragma unroll
+    for (int k = 0; k < KDEPTH; ++k) kpre[k] = bf16x8_t{};
+    int idx_cur = 0;               // slot for the gather of block b+3
     if (b_begin < b_end) {
-      if (wave == 0) {
-        issue_idx(b_begin);
-        if (b_begin + 1 < b_end) issue_idx(b_begin + 1);
+      const int b0 = b_begin;
+      int i0 = load_idx(b0);
+      int i1 = b0 + 1 < b_end ? load_idx(b0 + 1) : 0;
+      int i2 = b0 + 2 < b_end ? load_idx(b0 + 2) : 0;
+      idx_cur = b0 + 3 < b_end ? load_idx(b0 + 3) : 0;
+      // the four slot indices (once per segment); the wait names their
+      // registers so that nothing reading them is scheduled above it
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(i0), "+v"(i1), "+v"(i2), "+v"(idx_cur));
+      issue_data(b0, i0);
+      if (b0 + 1 < b_end) issue_data(b0 + 1, i1);
+      if (b0 + 2 < b_end) {
+        issue_data(b0 + 2, i2);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW));  // blocks b0, b0+1 have landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      issue_data(b_begin, 0);
-    }
-
-    for (int b = b_begin; b < b_end; ++b) {
-      const int cur = (b - b_begin) & 1;
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's global->LDS copies have landed
-      __syncthreads();                // ... and everyone else's
-      if (wave == 0 && b + 2 < b_end) issue_idx(b + 2);
-      if (b + 1 < b_end) issue_data(b + 1, cur ^ 1);
-      const lds_char* buf = lds + cur * BUFB;
-
-      // ---- partial S^T = K[:, half] Q^T[half, :], fragments two k-steps ahead ----
-      f32x16_t s = f32x16_t{};
+      __builtin_amdgcn_s_barrier();
       if (pair_live) {
-        const lds_char* kb0 = buf + kbase + kin[0];
-        const lds_char* kb1 = buf + kbase + kin[1];
-        const lds_char* kb2 = buf + kbase + kin[2];
-        const lds_char* kb3 = buf + kbase + kin[3];
-        const int kh = KS_HALF * half;  // first global k-step of this half
-        auto kread = [&](int k) {      // k = local k-step 0..17
-          const int ks = kh + k;
-          const int e = ks & 3;
-          const lds_char* b4 = e == 0 ? kb0 : (e == 1 ? kb1 : (e == 2 ? kb2 : kb3));
-          return lds_read_b128(b4, 128 * (ks >> 2));
-        };
-        bf16x8_t a0 = kread(0);
-        bf16x8_t a1 = kread(1);
+        const lds_char* kb0 = lds + (b0 % NBUF) * BUFB + kofs0;
+        const lds_char* kb1 = lds + (b0 % NBUF) * BUFB + kofs1;
+        f32x16_t sp = f32x16_t{};
 #pragma unroll
-        for (int k = 0; k < KS_HALF; k += 2) {
-          bf16x8_t n0 = a0, n1 = a1;
-          if (k + 2 < KS_HALF) n0 = kread(k + 2);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[k], s, 0, 0, 0);
-          if (k + 3 < KS_HALF) n1 = kread(k + 3);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[k + 1], s, 0, 0, 0);
-          a0 = n0;
-          a1 = n1;
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int k = 0; k < KS_HALF; ++k)
+          sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_read_b128((k & 1 ? kb1 : kb0) + 1024 * k), qf[k], sp, 0, 0, 0);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          f32x4 v = {s[4 * k], s[4 * k + 1], s[4 * k + 2], s[4 * k + 3]};
-          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xmine + k * 1024) = v;
+          f32x4 x = {sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
+          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xch + xmine + k * 1024) = x;
         }
-      }
-      __syncthreads();  // both halves of every pair are in the exchange buffer
-      if (!pair_live) continue;
+        s_mine = sp;
+        const lds_char* nb0 = lds + ((b0 + 1) % NBUF) * BUFB + kofs0;
+        const lds_char* nb1 = lds + ((b0 + 1) % NBUF) * BUFB + kofs1;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(xpart + k * 1024);
-        s[4 * k] += v[0];
-        s[4 * k + 1] += v[1];
-        s[4 * k + 2] += v[2];
-        s[4 * k + 3] += v[3];
+        for (int k = 0; k < KDEPTH; ++k) kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 1024 * k);
       }
+      lds_barrier();
+    }
 
-      // ---- scale + mask ----
-      const int cb = b * KB;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] *= p.scale_log2;
-      if (cb + KB > g.P) {
-        const int jbase = cb - g.P;  // tree index of the block's column 0
-        const int w0 = jbase > 0 ? (jbase >> 5) : 0;
-        const uint32_t bw0 = w0 < p.W ? vrow[w0] : 0u;
-        const uint32_t bw1 = w0 + 1 < p.W ? vrow[w0 + 1] : 0u;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int col = cb + 8 * (v >> 2) + 4 * hl + (v & 3);
-          bool vis = col < g.N;
-          const int j = col - g.P;
-          if (vis && j >= 0) {
-            const uint32_t word = (j >> 5) == w0 ? bw0 : bw1;
-            vis = (word >> (j & 31)) & 1u;
-          }
-          if (!vis) s[v] = -INFINITY;
-        }
-      }
+    // ------------------------------------------------------------------
+    // Iteration b.  Entry: blocks b, b+1 resident, b+2 in flight; this
+    // wave's half of S(b) in s_mine, the partner's in the exchange buffer;
+    // the first KDEPTH score fragments of block b+1 in kpre.
+    // Each MFMA below is one scheduling step (sched_barrier on both sides),
+    // with a hand-placed share of the other work underneath it.
+    // ------------------------------------------------------------------
+    auto step = [&](int b, auto tail_tag) {
+      constexpr bool TAIL = decltype(tail_tag)::value;
+      // 1. slot of block b+4, gather of block b+3 (into the buffer of block
+      //    b-1, whose last reader finished before the previous barrier)
+      int idx_next = 0;
+      if (b + 4 < b_end) idx_next = load_idx(b + 4);
+      if (b + 3 < b_end) issue_data(b + 3, idx_cur);
+      const int bufc = (b % NBUF) * BUFB;        // block b: values
+      const int bufn = ((b + 1) % NBUF) * BUFB;  // block b+1: scores (stale if none)
+      const int bufnn = ((b + 2) % NBUF) * BUFB; // block b+2: first fragments for the next step
 
-      // ---- online softmax (base 2) ----
-      float mb = max16(s);
-      mb = fmaxf(mb, other_half(mb));
-      const float m_new = fmaxf(m_run, mb);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      float psum = 0.f;
-      bf16x8_t pk[2];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = exp2f(s[v] - m_use);
+      f32x16_t sp = f32x16_t{};
+      bf16x8_t pk0, pk1, vf[2 * FB_HALF];
+      float psum = 0.f, m_use = 0.f, mb = 0.f;
+      bool move = false;
+      f32x16_t s;
+      const lds_char* vb0 = lds + bufc + vofs0;
+      const lds_char* vb1 = lds + bufc + vofs1;
+      auto vread = [&](int i) {  // value MFMA i: output block i & 7, column half i >> 3
+        const int off = 2048 * (i & 7) + 256 * (i >> 3);
+        const bf16x4_t lo = lds_read_tr(vb0 + off);
+        const bf16x4_t hi = lds_read_tr(vb1 + off);
+        return (bf16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      auto expo = [&](int x) {  // weight of score x under the current reference
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[x], c, -m_use));
         psum += e;
-        pk[v >> 3][v & 7] = (__bf16)e;
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__ballot(alpha != 1.f) != 0) {  // wave-uniform: skip when no row's max moved
+        return e;
+      };
+      if (pair_live) {
+        // 2. phase A: the 18 score MFMAs of block b+1.  Underneath: S(b) =
+        //    own half + partner's half, mask, block max, reference check,
+        //    weights of the lane's first 8 columns.
+        f32x4 xp[4];
 #pragma unroll
-        for (int fb = 0; fb < FB_HALF; ++fb) o[fb] *= alpha;
-      }
-
-      // ---- O^T[half] += V^T[half] P^T, fragments one feature block ahead ----
-      {
-        const int fh = 4 * half;  // (fb >> 1) offset of this half's features
-        const lds_char* vb00 = buf + vbase + vin00 + 128 * fh;
-        const lds_char* vb01 = buf + vbase + vin01 + 128 * fh;
-        const lds_char* vb10 = buf + vbase + 8 * ROWB + vin10 + 128 * fh;
-        const lds_char* vb11 = buf + vbase + 8 * ROWB + vin11 + 128 * fh;
-        auto vread = [&](int fb, int k2) {  // fb = local block 0..7
-          const int off = 128 * (fb >> 1) + 16 * k2 * ROWB;
-          const bf16x4_t lo = lds_read_tr((fb & 1) ? vb01 : vb00, off);
-          const bf16x4_t hi = lds_read_tr((fb & 1) ? vb11 : vb10, off);
-          return (bf16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-        bf16x8_t c0 = vread(0, 0), c1 = vread(0, 1);
+        for (int k = 0; k < 4; ++k)
+          xp[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              xch + xpart + k * 1024);
+        const lds_char* kb0 = lds + bufn + kofs0;
+        const lds_char* kb1 = lds + bufn + kofs1;
+        bf16x8_t kf[KS_HALF];
 #pragma unroll
-        for (int fb = 0; fb < FB_HALF; ++fb) {
-          bf16x8_t n0 = c0, n1 = c1;
-          if (fb + 1 < FB_HALF) n0 = vread(fb + 1, 0);
-          o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, pk[0], o[fb], 0, 0, 0);
-          if (fb + 1 < FB_HALF) n1 = vread(fb + 1, 1);
-          o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, pk[1], o[fb], 0, 0, 0);
-          c0 = n0;
-          c1 = n1;
+        for (int k = 0; k < KDEPTH; ++k) kf[k] = kpre[k];
+        float mx0 = 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < KS_HALF; ++k) {
+          if (k + KDEPTH < KS_HALF)
+            kf[k + KDEPTH] = lds_read_b128(((k + KDEPTH) & 1 ? kb1 : kb0) + 1024 * (k + KDEPTH));
+          sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], sp, 0, 0, 0);
+          if (k >= 1 && k <= 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[4 * (k - 1) + e] = s_mine[4 * (k - 1) + e] + xp[k - 1][e];
+          }
+          if (TAIL && k == 5) {
+            // mask: one 32-bit word, bit c = column cb + c visible
+            const int cb = b * KB;
+            const int jbase = cb - g.P;  // tree index of the block's column 0
+            uint32_t m32;
+            if (jbase >= 0) {
+              const int w0 = jbase >> 5, sh = jbase & 31;
+              uint32_t lo, hi;
+              if (p.W <= 4) {
+                lo = w0 == 0 ? vw[0] : (w0 == 1 ? vw[1] : (w0 == 2 ? vw[2] : vw[3]));
+                hi = w0 == 0 ? vw[1] : (w0 == 1 ? vw[2] : (w0 == 2 ? vw[3] : 0u));
+              } else {  // trees of more than 128 nodes
+                lo = w0 < p.W ? vrow[w0] : 0u;
+                hi = w0 + 1 < p.W ? vrow[w0 + 1] : 0u;
+              }
+              m32 = sh == 0 ? lo : (lo >> sh) | (hi << (32 - sh));
+            } else {  // prefix columns 0 .. -jbase-1, then tree nodes 0, 1, ...
+              const int np = -jbase;
+              m32 = (0xffffffffu >> (32 - np)) | (vw[0] << np);
+            }
+            const int ncol = g.N - cb;  // columns of the block that exist
+            if (ncol < 32) m32 &= (1u << ncol) - 1u;
+            // lane l holds columns 8 (x >> 2) + 4 (l >> 5) + (x & 3)
+            const uint32_t mine = m32 >> (4 * hl);
+#pragma unroll
+            for (int x = 0; x < 16; ++x)
+              if (!((mine >> (8 * (x >> 2) + (x & 3))) & 1u)) s[x] = -INFINITY;
+          }
+          if (k == 6)
+            mx0 = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                        fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+          if (k == 7) {
+            const float mx1 = fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                                    fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15])));
+            mb = fmaxf(mx0, mx1);
+          }
+          if (k == 8) {
+            mb = fmaxf(mb, other_half(mb)) * c;  // c > 0
+            // Online softmax reference in base 2, moved lazily: m_run
+            // changes only when the block max exceeds it by RESCALE_SLACK
+            // (log2 units), so the accumulator rescale is rare and weights
+            // stay below 2^RESCALE_SLACK.  O and l share the reference, so
+            // the result is exact.
+            constexpr float RESCALE_SLACK = 8.f;
+            move = mb > m_run + RESCALE_SLACK;  // also true while m_run is -inf
+            m_use = m_run == -INFINITY ? 0.f : m_run;  // all columns masked so far
+          }
+          if (k >= 9 && k <= 16) {
+            const int x = k - 9;
+            pk0[x] = (__bf16)expo(x);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
+
+        // 3. rare: the reference moves -- rescale O and l, redo the weights
+        if (__ballot(move) != 0) {  // wave-uniform
+          const float m_new = move ? mb : m_run;
+          // rows that keep their reference get exactly 1 (also when it is still -inf)
+          const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+          // The accumulators live in AGPRs; pinning them there on both sides
+          // of the multiply keeps the compiler from moving all 128 of them
+          // into VGPRs for the rest of the loop.
+#pragma unroll
+          for (int fb = 0; fb < FB_HALF; ++fb) {
+            f32x16_t t = o[fb];
+            asm volatile("" : "+a"(t));
+            t *= alpha;
+            asm volatile("" : "+a"(t));
+            o[fb] = t;
+          }
+          m_run = m_new;
+          m_use = m_run == -INFINITY ? 0.f : m_run;
+          psum = 0.f;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) pk0[x] = (__bf16)expo(x);
+        }
+        // first value fragments of block b (resident since two steps ago)
+#pragma unroll
+        for (int i = 0; i < VDEPTH; ++i) vf[i] = vread(i);
       }
-    }
+
+      // 4. block b+2 has landed (only block b+3's gather may still run) and
+      //    everyone has read the exchange buffer before it is rewritten
+      //    (the wait names idx_next: its consumers stay below it)
+      __builtin_amdgcn_sched_barrier(0);
+      if (b + 3 < b_end) {
+        asm volatile("s_waitcnt vmcnt(%1) lgkmcnt(0)" : "+v"(idx_next) : "i"(LPW));
+      } else {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : "+v"(idx_next));
+      }
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+
+      if (pair_live) {
+        // 5. phase B: O^T[half] += V^T[half] P^T for block b, column half 0
+        //    first.  Underneath: the weights of the lane's last 8 columns,
+        //    the hand-off of S(b+1)'s half, the first score fragments of b+2.
+        const lds_char* nb0 = lds + bufnn + kofs0;
+        const lds_char* nb1 = lds + bufnn + kofs1;
+#pragma unroll
+        for (int i = 0; i < 2 * FB_HALF; ++i) {
+          if (i + VDEPTH < 2 * FB_HALF) vf[i + VDEPTH] = vread(i + VDEPTH);
+          o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], i < 8 ? pk0 : pk1, o[i & 7], 0,
+                                                              0, 0);
+          if (i < 8) pk1[i] = (__bf16)expo(8 + i);
+          if (i >= 8 && i < 12) {
+            const int k = i - 8;
+            f32x4 x = {sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
+            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xch + xmine + k * 1024) = x;
+          }
+          if (i >= 12 && i < 12 + KDEPTH) {
+            const int k = i - 12;
+            kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 1024 * k);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run += psum;
+        s_mine = sp;
+      }
+
+      // 6. the hand-off is visible
+      lds_barrier();
+      idx_cur = idx_next;
+    };
+
+    // blocks that lie wholly inside the prefix need no mask
+    const int b_mask = max(b_begin, min(b_end, g.P / KB));
+    for (int b = b_begin; b < b_mask; ++b) step(b, std::integral_constant<bool, false>{});
+    for (int b = b_mask; b < b_end; ++b) step(b, std::integral_constant<bool, true>{});
 
     // ---- write this segment (rows of the pair, features of the half) ----
     const float l_tot = l_run + other_half(l_run);
