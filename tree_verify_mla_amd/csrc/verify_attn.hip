@@ -96,15 +96,35 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Params p) {
   }
 }
 
-// One workgroup per row tile: combine the tile's partial slots.
-__global__ __launch_bounds__(256) void merge_kernel(Params p, int mt, int G, int dtype) {
-  const int tile = blockIdx.x;
+// Merge of a tile's partial slots: one workgroup per (tile, MERGE_ROWS-row
+// group), wave w owning row w of the group for the statistics.  The slot
+// list and the per-segment weights 2^(m_s - M) are computed once per
+// segment and kept in LDS; the weighted sum of the partial outputs is then
+// a streaming pass (consecutive threads read consecutive float4s of a row).
+constexpr int MERGE_ROWS = 4;    // rows per merge workgroup (= waves)
+constexpr int MERGE_CHUNK = 512; // segments staged in LDS at a time
+
+// workspace slot of segment k of tile t of request r
+__device__ inline long long merge_slot(const Params& p, long long k, long long first_slot,
+                                       long long w_first, long long tile_start, long long U,
+                                       long long Ge) {
+  if (p.S > 0) return first_slot + k;
+  const long long w = w_first + k;
+  return 2 * w + (range_begin(w, U, Ge) >= tile_start ? 0 : 1);
+}
+
+__global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt, int G, int dtype) {
+  const int groups = (mt + MERGE_ROWS - 1) / MERGE_ROWS;
+  const int tile = blockIdx.x / groups, rg = blockIdx.x % groups;
   const int r = tile / p.T_max, t = tile % p.T_max;
   if (r >= p.bs) return;
   const Geom g = geom(p.qo, p.kvp, r, p.H, mt);
   if (t >= g.T) return;
+  const int row0 = rg * MERGE_ROWS;                 // first row of the group inside the tile
+  const int rows = min(MERGE_ROWS, g.R - t * mt - row0);
+  if (rows <= 0) return;
   long long first_slot = 0, w_first = 0, tile_start = 0, U = 0, Ge = 1;
-  int nseg;
+  long long nseg;
   if (p.S > 0) {
     nseg = p.S;
     first_slot = ((long long)r * p.T_max + t) * p.S;
@@ -116,60 +136,87 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p, int mt, int G, int
     w_first = group_of(tile_start, U, Ge);
     const long long w_last = group_of(tile_start + g.NB - 1, U, Ge);
     if (w_first == w_last) return;  // one workgroup covered the tile and wrote it
-    nseg = (int)(w_last - w_first + 1);
+    nseg = w_last - w_first + 1;
   }
-  const int rows = min(mt, g.R - t * mt);
   const long long sf = slot_floats(mt);
-  for (int idx = threadIdx.x; idx < rows * (DV / 4); idx += blockDim.x) {
-    const int row = idx / (DV / 4);
-    const int f4 = (idx % (DV / 4)) * 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  __shared__ long long s_slot[MERGE_CHUNK];
+  __shared__ float s_w[MERGE_CHUNK][MERGE_ROWS];
+  __shared__ float s_M[MERGE_ROWS], s_L[MERGE_ROWS];
+
+  // pass 1: running max of each row over all segments (wave = row)
+  if (wave < rows) {
     float M = -INFINITY;
-    for (int k = 0; k < nseg; ++k) {
-      long long slot;
-      if (p.S > 0) {
-        slot = first_slot + k;
-      } else {
-        const long long w = w_first + k;
-        slot = 2 * w + (range_begin(w, U, Ge) >= tile_start ? 0 : 1);
-      }
-      M = fmaxf(M, p.ws[slot * sf + (long long)mt * DV + row]);
+    for (long long k = lane; k < nseg; k += 64) {
+      const long long slot = merge_slot(p, k, first_slot, w_first, tile_start, U, Ge);
+      M = fmaxf(M, p.ws[slot * sf + (long long)mt * DV + row0 + wave]);
     }
-    float L = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int k = 0; k < nseg; ++k) {
-      long long slot;
-      if (p.S > 0) {
-        slot = first_slot + k;
-      } else {
-        const long long w = w_first + k;
-        slot = 2 * w + (range_begin(w, U, Ge) >= tile_start ? 0 : 1);
-      }
-      const float* base = p.ws + slot * sf;
-      const float ms = base[(long long)mt * DV + row];
-      const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      L = fmaf(wgt, base[(long long)mt * DV + mt + row], L);
-      const float4 ov = *reinterpret_cast<const float4*>(base + (long long)row * DV + f4);
-      a0 = fmaf(wgt, ov.x, a0);
-      a1 = fmaf(wgt, ov.y, a1);
-      a2 = fmaf(wgt, ov.z, a2);
-      a3 = fmaf(wgt, ov.w, a3);
-    }
-    const float inv = 1.f / L;
-    const size_t orow = (size_t)g.q0 * p.H + (size_t)t * mt + row;
-    if (dtype == DDTREE_BF16) {
-      __bf16* out = static_cast<__bf16*>(p.out) + orow * DV + f4;
-      out[0] = (__bf16)(a0 * inv);
-      out[1] = (__bf16)(a1 * inv);
-      out[2] = (__bf16)(a2 * inv);
-      out[3] = (__bf16)(a3 * inv);
-    } else {
-      float* out = static_cast<float*>(p.out) + orow * DV + f4;
-      out[0] = a0 * inv;
-      out[1] = a1 * inv;
-      out[2] = a2 * inv;
-      out[3] = a3 * inv;
-    }
-    if (f4 == 0 && p.lse) p.lse[orow] = (M + log2f(L)) * LN2;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0) s_M[wave] = M;
   }
+  __syncthreads();
+
+  // pass 2: weights and weighted sums, MERGE_CHUNK segments at a time
+  const int row = tid / (DV / 4 / 2);  // 64 threads x 2 float4 = one row of 512
+  const int f4 = (tid % (DV / 4 / 2)) * 4;  // first of this thread's two float4s: f4, f4 + 256
+  float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
+  float lsum = 0.f;
+  for (long long k0 = 0; k0 < nseg; k0 += MERGE_CHUNK) {
+    const int cnt = (int)min((long long)MERGE_CHUNK, nseg - k0);
+    for (int k = tid; k < cnt; k += blockDim.x)
+      s_slot[k] = merge_slot(p, k0 + k, first_slot, w_first, tile_start, U, Ge);
+    __syncthreads();
+    if (wave < rows) {
+      const float M = s_M[wave];
+      for (int k = lane; k < cnt; k += 64) {
+        const float* base = p.ws + s_slot[k] * sf + (long long)mt * DV;
+        const float ms = base[row0 + wave];
+        const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+        s_w[k][wave] = wgt;
+        lsum = fmaf(wgt, base[mt + row0 + wave], lsum);
+      }
+    }
+    __syncthreads();
+    if (row < rows) {
+      for (int k = 0; k < cnt; ++k) {
+        const float wgt = s_w[k][row];
+        const float* o = p.ws + s_slot[k] * sf + (long long)(row0 + row) * DV;
+        const float4 a = *reinterpret_cast<const float4*>(o + f4);
+        const float4 b = *reinterpret_cast<const float4*>(o + f4 + DV / 2);
+        acc0.x = fmaf(wgt, a.x, acc0.x); acc0.y = fmaf(wgt, a.y, acc0.y);
+        acc0.z = fmaf(wgt, a.z, acc0.z); acc0.w = fmaf(wgt, a.w, acc0.w);
+        acc1.x = fmaf(wgt, b.x, acc1.x); acc1.y = fmaf(wgt, b.y, acc1.y);
+        acc1.z = fmaf(wgt, b.z, acc1.z); acc1.w = fmaf(wgt, b.w, acc1.w);
+      }
+    }
+    __syncthreads();  // s_slot / s_w are rewritten by the next chunk
+  }
+  if (wave < rows) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+    if (lane == 0) s_L[wave] = lsum;
+  }
+  __syncthreads();
+  if (row >= rows) return;
+  const float L = s_L[row], inv = 1.f / L;
+  const size_t orow = (size_t)g.q0 * p.H + (size_t)t * mt + row0 + row;
+  const float o8[8] = {acc0.x * inv, acc0.y * inv, acc0.z * inv, acc0.w * inv,
+                       acc1.x * inv, acc1.y * inv, acc1.z * inv, acc1.w * inv};
+  if (dtype == DDTREE_BF16) {
+    __bf16* out = static_cast<__bf16*>(p.out) + orow * DV;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[f4 + e] = (__bf16)o8[e];
+      out[f4 + DV / 2 + e] = (__bf16)o8[4 + e];
+    }
+  } else {
+    float* out = static_cast<float*>(p.out) + orow * DV;
+    *reinterpret_cast<float4*>(out + f4) = make_float4(o8[0], o8[1], o8[2], o8[3]);
+    *reinterpret_cast<float4*>(out + f4 + DV / 2) = make_float4(o8[4], o8[5], o8[6], o8[7]);
+  }
+  if (f4 == 0 && p.lse) p.lse[orow] = (s_M[row] + log2f(L)) * LN2;
 }
 
 }  // namespace
@@ -180,9 +227,9 @@ int launch_f32(const Params& p, int grid, hipStream_t s) {
 }
 
 int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s) {
-  const long long tiles = (long long)p.bs * p.T_max;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)tiles), dim3(256), 0, s, p, mt, grid_groups,
-                     dtype);
+  const long long groups = (long long)p.bs * p.T_max * ((mt + MERGE_ROWS - 1) / MERGE_ROWS);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)groups), dim3(64 * MERGE_ROWS), 0, s, p, mt,
+                     grid_groups, dtype);
   return check_launch("verify_attn(merge)");
 }
 
@@ -239,8 +286,9 @@ extern "C" int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t nu
                  "verify_attn: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   const int mt = dtype == DDTREE_BF16 ? MT_BF16 : MT_F32;
   const long long T_max = ((long long)max_q_len * num_heads + mt - 1) / mt;
-  DDTREE_REQUIRE(T_max * bs * (num_splits > 0 ? num_splits : 1) < (1LL << 31), DDTREE_EUNSUPPORTED,
-                 "verify_attn: grid too large");
+  DDTREE_REQUIRE(T_max * bs * (num_splits > 0 ? num_splits : 1) < (1LL << 31) &&
+                     T_max * bs * ((mt + MERGE_ROWS - 1) / MERGE_ROWS) < (1LL << 31),
+                 DDTREE_EUNSUPPORTED, "verify_attn: grid too large");
 
   Params p;
   p.q = q;

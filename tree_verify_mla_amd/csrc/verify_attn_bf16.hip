@@ -27,21 +27,23 @@
 // Splitting the pair this way keeps each LDS byte feeding 32 rows while a
 // wave needs only 72 VGPRs of queries and 128 accumulators of output.
 //
-// Block buffer layout.  A block is 32 latent rows x 72 chunks of 16 bytes.
-// The buffer is 36 groups of 1 KB; group j holds chunks 2j and 2j+1 of all
-// 32 rows, chunk 2j+q of row r at 16-byte position
-//   pos(r, q, j) = 16 * ((r >> 4) + 2q) + ((r + 4q + 8 * (j & 1)) & 15).
-// * gather: one global_load_lds_dwordx4 fills one group (lane = position);
-//   the waves of one parity of j see the same (row, q) per lane, so a lane
-//   computes one pool address per block and adds 32 * j per load.
+// Block buffer layout.  A block is 32 latent rows x 72 chunks of 16 bytes,
+// stored as 36 groups of 1 KB: group 2m + h holds chunks 4m .. 4m+3 of rows
+// 16h .. 16h+15, and 16-byte position 4u + v of the group holds chunk
+// 4m + ((v - (u >> 2)) & 3) of row 16h + u.
+// * gather: one global_load_lds_dwordx4 fills one group (lane = position).
+//   Each 4-lane quad reads one 64-byte span of one row (a quarter of the
+//   lanes' cache lines, coalesced), and wave w fetches rows 16 (w & 1) + l/4,
+//   features [288 (w >> 1), +288) of them: one pool address per lane and
+//   block, the 64-byte steps in the instruction's immediate offset.
 // * score fragment (k-step j, lane l: row l & 31, chunk 2j + (l >> 5)): two
-//   base addresses (j even / odd) plus an immediate 1 KB * j.
+//   base addresses (j even / odd) plus an immediate 2 KB * (j >> 1).
 // * transposed value fragments (4 rows x 16 features per 16 lanes): two
 //   base addresses plus immediates.
 // gfx950 LDS has 64 four-byte banks; a b128 read is serviced 16 lanes at a
-// time, a b64 (and the transposing b64) read 32 lanes at a time.  In both
-// patterns the lanes of one phase land on 16 distinct positions mod 16, so
-// neither has bank conflicts.
+// time, a b64 (and the transposing b64) read 32 lanes at a time.  The
+// rotation by (u >> 2) puts the lanes of each phase of both patterns on 16
+// distinct 16-byte positions mod 256 bytes, so neither has bank conflicts.
 //
 // Pipeline: four block buffers, two blocks in flight.  Iteration b holds the
 // partial scores of block b; it starts the gather of block b+3, completes
@@ -76,9 +78,6 @@ constexpr float LN2 = 0.693147180559945309f;
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
 constexpr int WAIT_LGKM0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
 
-__device__ inline int chunk_pos(int r, int q, int jodd) {
-  return 16 * ((r >> 4) + 2 * q) + ((r + 4 * q + 8 * jodd) & 15);
-}
 
 // Workgroup barrier that waits only for this wave's LDS traffic, leaving the
 // global->LDS gathers of later blocks in flight (__syncthreads() would wait
@@ -99,10 +98,22 @@ __device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 // reads.  Ordering is explicit instead: every consumer of a gathered block
 // or of a loaded index sits behind an s_waitcnt vmcnt that retires it.
 // The "memory" clobber keeps all other memory accesses on their side.
-__device__ inline void gather16(const char* src, const lds_char* dst) {
-  // 16 bytes per lane: LDS address = M0 + 16 * lane
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"((unsigned)(size_t)dst)
+// 16 bytes per lane from src + OFS into LDS at dst + 16 * lane.  The
+// instruction's immediate offset applies to both addresses, so M0 carries
+// dst - OFS and one address register serves every load of a block.
+template <int OFS>
+__device__ inline void gather16(const char* src, unsigned dst) {
+  static_assert(OFS >= 0 && OFS < 4096, "immediate offset range");
+  asm volatile("global_load_lds_dwordx4 %0, off offset:%2" ::"v"(src), "{m0}"(dst - OFS), "i"(OFS)
                : "memory");
+}
+
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 __device__ inline int load_async(const int32_t* ptr) {
   // the result may be read only after an s_waitcnt that retires this load
@@ -145,7 +156,7 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
   constexpr int MT = 16 * NW;
   static_assert(MT == MT_BF16, "tile rows must match the schedule");
-  static_assert(NW % 2 == 0 && LOADS % NW == 0, "gather groups must split evenly by parity");
+  static_assert(NW == 4, "the block layout splits the gather over 2 x 2 waves");
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUFB + NW * XCH];
   lds_char* lds = (lds_char*)smem;  // generic -> LDS address space
   lds_char* xch = lds + NBUF * BUFB;
@@ -160,23 +171,29 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
   const int xpart = (wave ^ 1) * XCH + lane * 16;
 
   // ---- lane constants of the buffer layout (header comment) ----
-  // score fragments: k-step 18 * half + k at kofs[k & 1] + 1024 * k
-  const int kofs0 = KS_HALF * 1024 * half + 16 * chunk_pos(l32, hl, 0);
-  const int kofs1 = KS_HALF * 1024 * half + 16 * chunk_pos(l32, hl, 1);
+  // score fragments: k-step 18 * half + k at kofs[k & 1] + 2048 * (k >> 1)
+  // (row l32 = 16 (l32 >> 4) + u, chunk 2 k-step + hl)
+  int kofs0, kofs1;
+  {
+    const int u = l32 & 15;
+    const int kb = KS_HALF * 1024 * half + 1024 * (l32 >> 4) + 64 * u;
+    kofs0 = kb + 16 * ((hl + (u >> 2)) & 3);
+    kofs1 = kb + 16 * ((2 + hl + (u >> 2)) & 3);
+  }
   // value fragments of output block fb, column half k2, row quad t at
-  // vofs[t] + 2048 * fb + 256 * k2: 16-lane group g supplies block rows
-  // 16 k2 + 8 t + 4 (l >> 5) + (c >> 2) and features 16 (g & 1) + 4 (c & 3) .. +3
+  // vofs[t] + 2048 * fb + 1024 * k2: in 16-lane group g, lane c supplies block
+  // row 16 k2 + 8 t + 4 (l >> 5) + (c >> 2), features 16 (g & 1) + 4 (c & 3) .. +3
   int vofs0, vofs1;
   {
-    const int g16 = lane >> 4, cq = lane & 15, q = (cq & 3) >> 1;
-    const int x0 = (4 * hl + (cq >> 2) + 4 * q + 8 * (g16 & 1)) & 15;
-    const int vb = 16 * 1024 * half + 1024 * (g16 & 1) + 512 * q + 8 * (cq & 1);
-    vofs0 = vb + 16 * x0;
-    vofs1 = vb + 16 * (x0 ^ 8);
+    const int g16 = lane >> 4, cq = lane & 15;
+    const int cp = 2 * (g16 & 1) + ((cq & 3) >> 1);  // chunk inside the group's 4
+    const int vb = 16 * 1024 * half + 64 * (4 * hl + (cq >> 2)) + 8 * (cq & 1);
+    vofs0 = vb + 16 * ((cp + hl) & 3);
+    vofs1 = vb + 512 + 16 * ((cp + 2 + hl) & 3);
   }
-  // gather: the block row and chunk parity this lane fetches (groups of parity `half`)
-  const int grow = 16 * ((lane >> 4) & 1) + (((lane & 15) - 4 * (lane >> 5) - 8 * half) & 15);
-  const int gq16 = 16 * (lane >> 5);
+  // gather: the block row this lane fetches and its byte offset in the row
+  const int grow = 16 * half + (lane >> 2);
+  const int gofs = 16 * (((lane & 3) - (lane >> 4)) & 3) + 576 * (wave >> 1);
 
   // ---- schedule ----
   // Persistent: G workgroups take equal contiguous ranges of the unit list.
@@ -290,15 +307,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     const int32_t* kvi = p.kvi + g.kv0;
     auto load_idx = [&](int b) { return load_async(kvi + min(b * KB + grow, g.N - 1)); };
     // this wave's share of the gather of block b: groups j = wave, wave + NW, ...
+    // (load i fills group 2 (9 (wave >> 1) + i) + (wave & 1) from row offset gofs + 64 i)
+    const unsigned lds0 = (unsigned)(size_t)lds + 18432u * (wave >> 1) + 1024u * (wave & 1);
     auto issue_data = [&](int b, int sid) {
       sid = min(max(sid, 0), nslot_m1);
-      const char* src = poolb + (long long)sid * ROWB + gq16;
-      lds_char* dst = lds + (b % NBUF) * BUFB;
-#pragma unroll
-      for (int i = 0; i < LOADS / NW; ++i) {
-        const int j = wave + NW * i;
-        gather16(src + 32 * j, dst + 1024 * j);
-      }
+      const char* src = poolb + (long long)sid * ROWB + gofs;
+      const unsigned dst = lds0 + (unsigned)uni((b % NBUF) * BUFB);
+      static_for<0, LOADS / NW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        gather16<64 * i>(src, dst + 2048u * i);
+      });
     };
     constexpr int LPW = LOADS / NW;  // gather loads per wave per block
     constexpr int KDEPTH = 4;        // score fragments read ahead (at most 4)
@@ -339,7 +357,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
 #pragma unroll
         for (int k = 0; k < KS_HALF; ++k)
           sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              lds_read_b128((k & 1 ? kb1 : kb0) + 1024 * k), qf[k], sp, 0, 0, 0);
+              lds_read_b128((k & 1 ? kb1 : kb0) + 2048 * (k >> 1)), qf[k], sp, 0, 0, 0);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           f32x4 x = {sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
@@ -349,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         const lds_char* nb0 = lds + ((b0 + 1) % NBUF) * BUFB + kofs0;
         const lds_char* nb1 = lds + ((b0 + 1) % NBUF) * BUFB + kofs1;
 #pragma unroll
-        for (int k = 0; k < KDEPTH; ++k) kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 1024 * k);
+        for (int k = 0; k < KDEPTH; ++k) kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 2048 * (k >> 1));
       }
       lds_barrier();
     }
@@ -361,7 +379,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     // Each MFMA below is one scheduling step (sched_barrier on both sides),
     // with a hand-placed share of the other work underneath it.
     // ------------------------------------------------------------------
-    auto step = [&](int b, auto tail_tag) {
+    auto step = [&](int b, auto tail_tag, f32x16_t& s_cur, f32x16_t& sp) {
       constexpr bool TAIL = decltype(tail_tag)::value;
       // 1. slot of block b+4, gather of block b+3 (into the buffer of block
       //    b-1, whose last reader finished before the previous barrier)
@@ -372,7 +390,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       const int bufn = ((b + 1) % NBUF) * BUFB;  // block b+1: scores (stale if none)
       const int bufnn = ((b + 2) % NBUF) * BUFB; // block b+2: first fragments for the next step
 
-      f32x16_t sp = f32x16_t{};
       bf16x8_t pk0, pk1, vf[2 * FB_HALF];
       float psum = 0.f, m_use = 0.f, mb = 0.f;
       bool move = false;
@@ -380,7 +397,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       const lds_char* vb0 = lds + bufc + vofs0;
       const lds_char* vb1 = lds + bufc + vofs1;
       auto vread = [&](int i) {  // value MFMA i: output block i & 7, column half i >> 3
-        const int off = 2048 * (i & 7) + 256 * (i >> 3);
+        const int off = 2048 * (i & 7) + 1024 * (i >> 3);
         const bf16x4_t lo = lds_read_tr(vb0 + off);
         const bf16x4_t hi = lds_read_tr(vb1 + off);
         return (bf16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -405,15 +422,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
 #pragma unroll
         for (int k = 0; k < KDEPTH; ++k) kf[k] = kpre[k];
         float mx0 = 0.f;
+        sp = f32x16_t{};
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < KS_HALF; ++k) {
           if (k + KDEPTH < KS_HALF)
-            kf[k + KDEPTH] = lds_read_b128(((k + KDEPTH) & 1 ? kb1 : kb0) + 1024 * (k + KDEPTH));
+            kf[k + KDEPTH] =
+                lds_read_b128(((k + KDEPTH) & 1 ? kb1 : kb0) + 2048 * ((k + KDEPTH) >> 1));
           sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], sp, 0, 0, 0);
           if (k >= 1 && k <= 4) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[4 * (k - 1) + e] = s_mine[4 * (k - 1) + e] + xp[k - 1][e];
+            for (int e = 0; e < 4; ++e) s[4 * (k - 1) + e] = s_cur[4 * (k - 1) + e] + xp[k - 1][e];
           }
           if (TAIL && k == 5) {
             // mask: one 32-bit word, bit c = column cb + c visible
@@ -528,12 +547,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
           }
           if (i >= 12 && i < 12 + KDEPTH) {
             const int k = i - 12;
-            kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 1024 * k);
+            kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 2048 * (k >> 1));
           }
           __builtin_amdgcn_sched_barrier(0);
         }
         l_run += psum;
-        s_mine = sp;
       }
 
       // 6. the hand-off is visible
@@ -541,10 +559,27 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       idx_cur = idx_next;
     };
 
-    // blocks that lie wholly inside the prefix need no mask
+    // Blocks that lie wholly inside the prefix need no mask.  The prefix
+    // loop is unrolled by two so the two score registers swap roles instead
+    // of being copied every block.
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
     const int b_mask = max(b_begin, min(b_end, g.P / KB));
-    for (int b = b_begin; b < b_mask; ++b) step(b, std::integral_constant<bool, false>{});
-    for (int b = b_mask; b < b_end; ++b) step(b, std::integral_constant<bool, true>{});
+    f32x16_t s_alt = f32x16_t{};
+    int b = b_begin;
+    for (; b + 1 < b_mask; b += 2) {
+      step(b, NoMask{}, s_mine, s_alt);
+      step(b + 1, NoMask{}, s_alt, s_mine);
+    }
+    if (b < b_mask) {
+      step(b, NoMask{}, s_mine, s_alt);
+      s_mine = s_alt;
+      ++b;
+    }
+    for (; b < b_end; ++b) {
+      step(b, Mask{}, s_mine, s_alt);
+      s_mine = s_alt;
+    }
 
     // ---- write this segment (rows of the pair, features of the half) ----
     const float l_tot = l_run + other_half(l_run);
