@@ -11,7 +11,7 @@ Each function is a plain, slow, obviously-correct statement of one stage:
                                  brute-force enumerator used to pin it;
 * ``visibility``                 ancestor-or-self visibility, full
                                  ``[q_len, prefix+q_len]`` mask and positions;
-* ``attention.verify_attention`` fp64 masked softmax over the absorbed-MLA
+* ``attention.verify_request``   fp64 masked softmax over the absorbed-MLA
                                  576-d latents, output = weighted c_kv;
 * ``accept.accept``              greedy root walk along the target argmax,
                                  plus a brute-force path enumerator.

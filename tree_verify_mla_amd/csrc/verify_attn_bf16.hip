@@ -91,23 +91,6 @@ __device__ inline void lds_barrier() {
 
 __device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// The gather and its slot-index loads are issued as inline asm so that the
-// compiler's wait-count model does not see them: it cannot tell the
-// global->LDS writes from the transposing LDS reads of other buffers and
-// would otherwise wait for every gather in flight before each of those
-// reads.  Ordering is explicit instead: every consumer of a gathered block
-// or of a loaded index sits behind an s_waitcnt vmcnt that retires it.
-// The "memory" clobber keeps all other memory accesses on their side.
-// 16 bytes per lane from src + OFS into LDS at dst + 16 * lane.  The
-// instruction's immediate offset applies to both addresses, so M0 carries
-// dst - OFS and one address register serves every load of a block.
-template <int OFS>
-__device__ inline void gather16(const char* src, unsigned dst) {
-  static_assert(OFS >= 0 && OFS < 4096, "immediate offset range");
-  asm volatile("global_load_lds_dwordx4 %0, off offset:%2" ::"v"(src), "{m0}"(dst - OFS), "i"(OFS)
-               : "memory");
-}
-
 template <int I, int N, typename F>
 __device__ inline void static_for(F&& f) {
   if constexpr (I < N) {
@@ -115,13 +98,6 @@ __device__ inline void static_for(F&& f) {
     static_for<I + 1, N>(f);
   }
 }
-__device__ inline int load_async(const int32_t* ptr) {
-  // the result may be read only after an s_waitcnt that retires this load
-  int v;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(ptr) : "memory");
-  return v;
-}
-
 __device__ inline long long uni64(long long x) {
   const int lo = __builtin_amdgcn_readfirstlane((int)(x & 0xffffffffLL));
   const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
@@ -305,21 +281,27 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     // slot of the block row this lane gathers in block b (a register load,
     // issued one block ahead of its use)
     const int32_t* kvi = p.kvi + g.kv0;
-    auto load_idx = [&](int b) { return load_async(kvi + min(b * KB + grow, g.N - 1)); };
+    auto load_idx = [&](int b) { return kvi[min(b * KB + grow, g.N - 1)]; };
     // this wave's share of the gather of block b: groups j = wave, wave + NW, ...
-    // (load i fills group 2 (9 (wave >> 1) + i) + (wave & 1) from row offset gofs + 64 i)
-    const unsigned lds0 = (unsigned)(size_t)lds + 18432u * (wave >> 1) + 1024u * (wave & 1);
-    auto issue_data = [&](int b, int sid) {
+    // Load i fills group 2 (9 (wave >> 1) + i) + (wave & 1) of buffer dst from row
+    // offset gofs + 64 i.  The immediate offset applies to the pool address and
+    // the LDS address alike, so the LDS base (M0) is given as target - 64 i.
+    const int wofs = 18432 * (wave >> 1) + 1024 * (wave & 1);
+    auto issue_data = [&](lds_char* dst, int sid) {
+      // The index is opaque here so that the clamp below (and with it the
+      // wait for the index load) cannot be hoisted to the load itself.
+      asm volatile("" : "+v"(sid));
       sid = min(max(sid, 0), nslot_m1);
       const char* src = poolb + (long long)sid * ROWB + gofs;
-      const unsigned dst = lds0 + (unsigned)uni((b % NBUF) * BUFB);
       static_for<0, LOADS / NW>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        gather16<64 * i>(src, dst + 2048u * i);
+        __builtin_amdgcn_global_load_lds(
+            src, reinterpret_cast<__attribute__((address_space(3))) void*>(dst + wofs + 1984 * i),
+            16, 64 * i, 0);
       });
     };
     constexpr int LPW = LOADS / NW;  // gather loads per wave per block
-    constexpr int KDEPTH = 4;        // score fragments read ahead (at most 4)
+    constexpr int KDEPTH = 4;        // score fragments read ahead
     constexpr int VDEPTH = 2;        // value MFMAs whose fragments are read ahead
 
     // ------------------------------------------------------------------
@@ -334,21 +316,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     int idx_cur = 0;               // slot for the gather of block b+3
     if (b_begin < b_end) {
       const int b0 = b_begin;
-      int i0 = load_idx(b0);
-      int i1 = b0 + 1 < b_end ? load_idx(b0 + 1) : 0;
-      int i2 = b0 + 2 < b_end ? load_idx(b0 + 2) : 0;
-      idx_cur = b0 + 3 < b_end ? load_idx(b0 + 3) : 0;
-      // the four slot indices (once per segment); the wait names their
-      // registers so that nothing reading them is scheduled above it
-      asm volatile("s_waitcnt vmcnt(0)" : "+v"(i0), "+v"(i1), "+v"(i2), "+v"(idx_cur));
-      issue_data(b0, i0);
-      if (b0 + 1 < b_end) issue_data(b0 + 1, i1);
-      if (b0 + 2 < b_end) {
-        issue_data(b0 + 2, i2);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW));  // blocks b0, b0+1 have landed
-      } else {
-        __builtin_amdgcn_s_waitcnt(0);
-      }
+      // The pipeline is straight-line: blocks past the segment's end are
+      // "gathered" too (a valid row, into a buffer nobody reads), so every
+      // wait below is one fixed count that the compiler can account for.
+      const int i0 = load_idx(b0);
+      const int i1 = load_idx(b0 + 1);
+      const int i2 = load_idx(b0 + 2);
+      idx_cur = load_idx(b0 + 3);
+      issue_data(lds + (b0 % NBUF) * BUFB, i0);
+      issue_data(lds + ((b0 + 1) % NBUF) * BUFB, i1);
+      issue_data(lds + ((b0 + 2) % NBUF) * BUFB, i2);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW));  // blocks b0, b0+1 have landed
       __builtin_amdgcn_s_barrier();
       if (pair_live) {
         const lds_char* kb0 = lds + (b0 % NBUF) * BUFB + kofs0;
@@ -379,23 +357,30 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     // Each MFMA below is one scheduling step (sched_barrier on both sides),
     // with a hand-placed share of the other work underneath it.
     // ------------------------------------------------------------------
-    auto step = [&](int b, auto tail_tag, f32x16_t& s_cur, f32x16_t& sp) {
+    // The four buffers an iteration touches are distinct, and the body says
+    // so with restrict pointers: that lets the compiler see that the
+    // transposing reads of block b cannot alias the gather into block b+3, so
+    // it does not wait for that gather before them.
+    //   dmab: block b+3 (gather target; held block b-1, whose last reader
+    //         finished before the previous barrier)
+    //   vbuf: block b (values)   kbuf: block b+1 (scores; stale if none)
+    //   nbuf: block b+2 (first score fragments of the next iteration)
+    auto body = [&](int b, auto tail_tag, f32x16_t& s_cur, f32x16_t& sp,
+                    lds_char* __restrict__ dmab, const lds_char* __restrict__ vbuf,
+                    const lds_char* __restrict__ kbuf, const lds_char* __restrict__ nbuf,
+                    lds_char* __restrict__ xb) {
       constexpr bool TAIL = decltype(tail_tag)::value;
-      // 1. slot of block b+4, gather of block b+3 (into the buffer of block
-      //    b-1, whose last reader finished before the previous barrier)
-      int idx_next = 0;
-      if (b + 4 < b_end) idx_next = load_idx(b + 4);
-      if (b + 3 < b_end) issue_data(b + 3, idx_cur);
-      const int bufc = (b % NBUF) * BUFB;        // block b: values
-      const int bufn = ((b + 1) % NBUF) * BUFB;  // block b+1: scores (stale if none)
-      const int bufnn = ((b + 2) % NBUF) * BUFB; // block b+2: first fragments for the next step
+      // 1. slot of block b+4, gather of block b+3 (past the end: a valid row
+      //    into a free buffer)
+      const int idx_next = load_idx(b + 4);
+      issue_data(dmab, idx_cur);
 
       bf16x8_t pk0, pk1, vf[2 * FB_HALF];
       float psum = 0.f, m_use = 0.f, mb = 0.f;
       bool move = false;
       f32x16_t s;
-      const lds_char* vb0 = lds + bufc + vofs0;
-      const lds_char* vb1 = lds + bufc + vofs1;
+      const lds_char* vb0 = vbuf + vofs0;
+      const lds_char* vb1 = vbuf + vofs1;
       auto vread = [&](int i) {  // value MFMA i: output block i & 7, column half i >> 3
         const int off = 2048 * (i & 7) + 1024 * (i >> 3);
         const bf16x4_t lo = lds_read_tr(vb0 + off);
@@ -415,9 +400,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           xp[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-              xch + xpart + k * 1024);
-        const lds_char* kb0 = lds + bufn + kofs0;
-        const lds_char* kb1 = lds + bufn + kofs1;
+              xb + xpart + k * 1024);
+        const lds_char* kb0 = kbuf + kofs0;
+        const lds_char* kb1 = kbuf + kofs1;
         bf16x8_t kf[KS_HALF];
 #pragma unroll
         for (int k = 0; k < KDEPTH; ++k) kf[k] = kpre[k];
@@ -518,13 +503,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
 
       // 4. block b+2 has landed (only block b+3's gather may still run) and
       //    everyone has read the exchange buffer before it is rewritten
-      //    (the wait names idx_next: its consumers stay below it)
       __builtin_amdgcn_sched_barrier(0);
-      if (b + 3 < b_end) {
-        asm volatile("s_waitcnt vmcnt(%1) lgkmcnt(0)" : "+v"(idx_next) : "i"(LPW));
-      } else {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : "+v"(idx_next));
-      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
 
@@ -532,8 +512,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         // 5. phase B: O^T[half] += V^T[half] P^T for block b, column half 0
         //    first.  Underneath: the weights of the lane's last 8 columns,
         //    the hand-off of S(b+1)'s half, the first score fragments of b+2.
-        const lds_char* nb0 = lds + bufnn + kofs0;
-        const lds_char* nb1 = lds + bufnn + kofs1;
+        const lds_char* nb0 = nbuf + kofs0;
+        const lds_char* nb1 = nbuf + kofs1;
 #pragma unroll
         for (int i = 0; i < 2 * FB_HALF; ++i) {
           if (i + VDEPTH < 2 * FB_HALF) vf[i + VDEPTH] = vread(i + VDEPTH);
@@ -543,10 +523,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
           if (i >= 8 && i < 12) {
             const int k = i - 8;
             f32x4 x = {sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
-            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xch + xmine + k * 1024) = x;
+            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xb + xmine + k * 1024) = x;
           }
-          if (i >= 12 && i < 12 + KDEPTH) {
-            const int k = i - 12;
+          if (i >= 2 * FB_HALF - KDEPTH) {
+            const int k = i - (2 * FB_HALF - KDEPTH);
             kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 2048 * (k >> 1));
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -557,6 +537,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       // 6. the hand-off is visible
       lds_barrier();
       idx_cur = idx_next;
+    };
+    auto step = [&](int b, auto tail_tag, f32x16_t& s_cur, f32x16_t& sp) {
+      body(b, tail_tag, s_cur, sp, lds + ((b + 3) % NBUF) * BUFB, lds + (b % NBUF) * BUFB,
+           lds + ((b + 1) % NBUF) * BUFB, lds + ((b + 2) % NBUF) * BUFB, xch);
     };
 
     // Blocks that lie wholly inside the prefix need no mask.  The prefix
