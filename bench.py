@@ -64,6 +64,43 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes": mib << 20, "copies": 5}), flush=True)
 
 
+ATTN_SOURCES = ("tree_verify_mla_amd/csrc/verify_attn_bf16.hip", "tree_verify_mla_amd/csrc/verify_attn.hip",
+                "tree_verify_mla_amd/csrc/attn_common.h")
+COUNTERS = os.path.join(ROOT, "profiles", "verify_attn_h64_bs8_q33_p8192_counters.txt")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention call from the committed counter summary, or None.
+
+    The summary holds FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the two
+    kernels of one call and of a plain copy of known size; the copy turns
+    the counters into bytes.  The figures count only while the attention
+    sources are the ones they were taken from."""
+    try:
+        with open(COUNTERS) as fh:
+            kv = dict(l.strip().split("=", 1) for l in fh if "=" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_sha256") != attn_source_hash() or kv.get("workload") != workload:
+        return None
+    copy_kib = float(kv["copy_bytes"]) / 1024.0
+    f_fac = copy_kib / float(kv["copy.FETCH_SIZE"])
+    w_fac = copy_kib / float(kv["copy.WRITE_SIZE"])
+    fetch = sum(float(kv[f"{k}.FETCH_SIZE"]) for k in ("attn_bf16_kernel", "merge_kernel"))
+    write = sum(float(kv[f"{k}.WRITE_SIZE"]) for k in ("attn_bf16_kernel", "merge_kernel"))
+    return {"fetch_bytes": fetch * 1024.0 * f_fac, "write_bytes": write * 1024.0 * w_fac,
+            "fetch_factor": f_fac, "write_factor": w_fac}
+
+
 def algorithmic_work(wl, depths):
     """(attention flops, attention bytes) the method itself needs for this batch."""
     H = wl.heads
@@ -83,34 +120,40 @@ def algorithmic_work(wl, depths):
     return flops, nbytes
 
 
-def cpu_baseline(wl, budget_s: float):
-    """The CPU oracle as it stands, on whole requests of the workload until the budget is used."""
+def cpu_baseline(wls, budget_s: float):
+    """The CPU oracle as it stands, on whole requests of the workload (cycling
+    through the rotated instances) until about budget_s seconds are used."""
     from threadpoolctl import threadpool_info
 
     from oracle import accept, attention, tree, visibility
     from workloads import draw_target_predict
 
     done, flops, t0 = 0, 0, time.perf_counter()
-    for r in range(wl.bs):
-        a, b = int(wl.qo_indptr[r]), int(wl.qo_indptr[r + 1])
-        t = tree.build_tree(wl.topk_logprobs[r], wl.topk_ids[r], int(wl.root_tokens[r]), b - a - 1)
-        P = int(wl.prefix_lens[r])
-        visibility.vis_bits(t.parents, (wl.max_q_len + 31) // 32)
-        visibility.positions(t.depths, P)
-        attention.verify_request(wl.q_f32()[a:b], wl.kv_rows_f32(wl.request_slots(r)), P,
-                                 t.parents, float(np.float32(wl.scale)))
-        pred = draw_target_predict(wl.seed, t.tokens, t.parents, np.array([0, b - a]), wl.vocab)
-        accept.accept(t.tokens, t.parents, pred, wl.depth)
-        flops += FLOP_PER_PAIR * wl.heads * ((b - a) * P + int((t.depths + 1).sum()))
-        done += 1
+    for wl in wls:
+        for r in range(wl.bs):
+            a, b = int(wl.qo_indptr[r]), int(wl.qo_indptr[r + 1])
+            t = tree.build_tree(wl.topk_logprobs[r], wl.topk_ids[r], int(wl.root_tokens[r]), b - a - 1)
+            P = int(wl.prefix_lens[r])
+            visibility.vis_bits(t.parents, (wl.max_q_len + 31) // 32)
+            visibility.positions(t.depths, P)
+            attention.verify_request(wl.q_f32()[a:b], wl.kv_rows_f32(wl.request_slots(r)), P,
+                                     t.parents, float(np.float32(wl.scale)))
+            pred = draw_target_predict(wl.seed, t.tokens, t.parents, np.array([0, b - a]), wl.vocab)
+            accept.accept(t.tokens, t.parents, pred, wl.depth)
+            flops += FLOP_PER_PAIR * wl.heads * ((b - a) * P + int((t.depths + 1).sum()))
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    total = sum(w.bs for w in wls)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {wl.bs} requests (tree + visibility + fp64 attention + accept), "
-                      f"{dt:.1f} s wall, {len(os.sched_getaffinity(0))} host cores visible",
+            "sample": f"{done} of {total} requests of the {len(wls)} rotated instances (tree + "
+                      f"visibility + fp64 attention + accept, whole requests), {dt:.1f} s wall, "
+                      f"{len(os.sched_getaffinity(0))} host cores visible",
             "tree_steps_per_s": done / dt}
 
 
@@ -188,6 +231,7 @@ def main():
     acc_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
 
     achieved = flops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic(wls[0].name)
     value = flops / (step_ms * 1e-3) / 1e12
     gbps = nbytes / (attn_ms * 1e-3) / 1e9
     line = {
@@ -209,15 +253,17 @@ def main():
                    "num_splits": args.num_splits, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "ddtree_verify_attn (attn_bf16_kernel + merge_kernel)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic is None else round(traffic["fetch_bytes"] + traffic["write_bytes"]),
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
+                     "traffic_detail": traffic},
         "extra": {"attn_ms": round(attn_ms, 5), "build_visibility_ms": round(tv_ms, 5),
                   "accept_ms": round(acc_ms, 5),
                   "attn_GBps": round(gbps, 1), "attn_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
                   "tree_steps_per_s": round(wls[0].bs / (step_ms * 1e-3), 1)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wls[0], args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wls, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
