@@ -9,6 +9,10 @@
 // Architecture: Confirming Multiple-Path Evaluation").  After k steps the
 // frontier holds at most k + 1 entries, so max_budget + 2 slots suffice.
 //
+// The request's per-depth log-probs and token ids are staged in LDS first:
+// the loop is a serial chain of budget steps, and a global load inside it
+// would add a full memory latency to every step.
+//
 // Order: higher fp32 score first, then smaller depth, then the
 // lexicographically smaller rank path.  Rank paths are packed big-endian in
 // 64 bits (rank_bits per depth), so equal-depth paths compare as integers.
@@ -46,6 +50,8 @@ __global__ __launch_bounds__(64) void build_tree_kernel(
   int* f_depth = reinterpret_cast<int*>(f_pscore + cap);
   int* f_rank = f_depth + cap;
   int* f_parent = f_rank + cap;
+  float* s_lp = reinterpret_cast<float*>(f_parent + cap);  // [D * K]
+  int32_t* s_id = reinterpret_cast<int32_t*>(s_lp + D * K);  // [D * K]
   __shared__ int n_front;
 
   const int r = blockIdx.x;
@@ -54,8 +60,17 @@ __global__ __launch_bounds__(64) void build_tree_kernel(
   const int Q = qo[r + 1] - base;
   if (Q < 1) return;
   const int B = min(Q - 1, max_budget);
-  const float* lpr = lp + (size_t)r * D * K;
-  const int32_t* idr = ids + (size_t)r * D * K;
+  if (B > 0) {
+    const float* lpg = lp + (size_t)r * D * K;
+    const int32_t* idg = ids + (size_t)r * D * K;
+    for (int i = lane; i < D * K; i += 64) {
+      s_lp[i] = lpg[i];
+      s_id[i] = idg[i];
+    }
+  }
+  __syncthreads();
+  const float* lpr = s_lp;
+  const int32_t* idr = s_id;
 
   for (int i = B + 1 + lane; i < Q; i += 64) {  // budget beyond max_budget
     tok[base + i] = -1;
@@ -186,7 +201,11 @@ extern "C" int ddtree_build_tree(const float* topk_logprobs, const int32_t* topk
                  (long long)depth_max * rank_bits);
   DDTREE_REQUIRE(max_budget <= 2048, DDTREE_EUNSUPPORTED,
                  "build_tree: max_budget %d above the supported 2048", max_budget);
-  const size_t lds = (size_t)(max_budget + 2) * (8 + 4 * 5);
+  DDTREE_REQUIRE(max_budget == 0 || (long long)depth_max * topk <= 8192, DDTREE_EUNSUPPORTED,
+                 "build_tree: depth_max * topk = %lld above the supported 8192",
+                 (long long)depth_max * topk);
+  const size_t staged = max_budget > 0 ? (size_t)depth_max * topk * 8 : 0;  // log-probs + ids
+  const size_t lds = (size_t)(max_budget + 2) * (8 + 4 * 5) + staged;
   hipLaunchKernelGGL(build_tree_kernel, dim3(bs), dim3(64), lds, ddtree::as_stream(stream),
                      topk_logprobs, topk_ids, root_tokens, qo_indptr, depth_max, topk, max_budget,
                      rank_bits, node_tokens, node_parents, node_depths, node_scores);

@@ -251,7 +251,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     // ---- this pair's 32 query rows; this wave's half of their features ----
     const int rho = t * MT + pair * 32 + l32;
     const bool row_ok = rho < g.R;
-    const bool pair_live = t * MT + pair * 32 < g.R;  // same for both waves of the pair
+    // A pair whose 32 rows all lie past the tile's end still runs the whole
+    // pipeline (on zero queries) so that every wave follows one straight-line
+    // path; the epilogue writes only rows < R.
     const int node = row_ok ? rho / p.H : g.Q - 1;
     bf16x8_t qf[KS_HALF];
     {
@@ -287,18 +289,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     // offset gofs + 64 i.  The immediate offset applies to the pool address and
     // the LDS address alike, so the LDS base (M0) is given as target - 64 i.
     const int wofs = 18432 * (wave >> 1) + 1024 * (wave & 1);
-    auto issue_data = [&](lds_char* dst, int sid) {
+    auto gather_src = [&](int sid) {
       // The index is opaque here so that the clamp below (and with it the
       // wait for the index load) cannot be hoisted to the load itself.
       asm volatile("" : "+v"(sid));
       sid = min(max(sid, 0), nslot_m1);
-      const char* src = poolb + (long long)sid * ROWB + gofs;
-      static_for<0, LOADS / NW>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        __builtin_amdgcn_global_load_lds(
-            src, reinterpret_cast<__attribute__((address_space(3))) void*>(dst + wofs + 1984 * i),
-            16, 64 * i, 0);
-      });
+      return poolb + (long long)sid * ROWB + gofs;
+    };
+    auto gather_one = [&](lds_char* dst, const char* src, auto ic) {
+      constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_global_load_lds(
+          src, reinterpret_cast<__attribute__((address_space(3))) void*>(dst + wofs + 1984 * i), 16,
+          64 * i, 0);
+    };
+    auto issue_data = [&](lds_char* dst, int sid) {
+      const char* src = gather_src(sid);
+      static_for<0, LOADS / NW>([&](auto ic) { gather_one(dst, src, ic); });
     };
     constexpr int LPW = LOADS / NW;  // gather loads per wave per block
     constexpr int KDEPTH = 4;        // score fragments read ahead
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       issue_data(lds + ((b0 + 2) % NBUF) * BUFB, i2);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW));  // blocks b0, b0+1 have landed
       __builtin_amdgcn_s_barrier();
-      if (pair_live) {
+      {
         const lds_char* kb0 = lds + (b0 % NBUF) * BUFB + kofs0;
         const lds_char* kb1 = lds + (b0 % NBUF) * BUFB + kofs1;
         f32x16_t sp = f32x16_t{};
@@ -370,10 +376,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
                     const lds_char* __restrict__ kbuf, const lds_char* __restrict__ nbuf,
                     lds_char* __restrict__ xb) {
       constexpr bool TAIL = decltype(tail_tag)::value;
-      // 1. slot of block b+4, gather of block b+3 (past the end: a valid row
-      //    into a free buffer)
+      // 1. gather of block b+3 (past the end: a valid row into a free
+      //    buffer), then the slot of block b+4.  The gather is spread over
+      //    the score MFMAs below so the address unit drains between loads.
+      //    Its address is formed
+      //    before the next index load, so no wait can cover that load.
+      const char* gsrc = gather_src(idx_cur);
       const int idx_next = load_idx(b + 4);
-      issue_data(dmab, idx_cur);
 
       bf16x8_t pk0, pk1, vf[2 * FB_HALF];
       float psum = 0.f, m_use = 0.f, mb = 0.f;
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         psum += e;
         return e;
       };
-      if (pair_live) {
+      {
         // 2. phase A: the 18 score MFMAs of block b+1.  Underneath: S(b) =
         //    own half + partner's half, mask, block max, reference check,
         //    weights of the lane's first 8 columns.
@@ -409,8 +418,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         float mx0 = 0.f;
         sp = f32x16_t{};
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < KS_HALF; ++k) {
+        static_for<0, KS_HALF>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          if constexpr (k % 2 == 1 && k / 2 < LPW)
+            gather_one(dmab, gsrc, std::integral_constant<int, k / 2>{});
           if (k + KDEPTH < KS_HALF)
             kf[k + KDEPTH] =
                 lds_read_b128(((k + KDEPTH) & 1 ? kb1 : kb0) + 2048 * ((k + KDEPTH) >> 1));
@@ -471,7 +482,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
             pk0[x] = (__bf16)expo(x);
           }
           __builtin_amdgcn_sched_barrier(0);
-        }
+        });
 
         // 3. rare: the reference moves -- rescale O and l, redo the weights
         if (__ballot(move) != 0) {  // wave-uniform
@@ -508,7 +519,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
 
-      if (pair_live) {
+      {
         // 5. phase B: O^T[half] += V^T[half] P^T for block b, column half 0
         //    first.  Underneath: the weights of the lane's last 8 columns,
         //    the hand-off of S(b+1)'s half, the first score fragments of b+2.
