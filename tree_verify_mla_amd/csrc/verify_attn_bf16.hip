@@ -1,41 +1,41 @@
 // bf16 verify attention on gfx950 matrix cores.
 //
-// Workgroup = NW wavefronts = one tile of 16*NW query rows of one request.
-// Waves pair up: both waves of pair g own the same 32 query rows; wave half
-// h contracts latent features [288h, 288h+288) of the score and produces
-// output features [256h, 256h+256).  The tile walks its KV columns in
-// blocks of 32; each block is gathered once from the slot pool into LDS and
-// shared by all rows -- the prefix is read once for every tree node and head
-// ("The DDTree CUDA Graph Fix ...", section "The DDTree Architecture:
-// Confirming Multiple-Path Evaluation").
+// Workgroup = NW = 4 wavefronts = one tile of 64 query rows of one request.
+// The tile walks its KV columns in blocks of 32; each block is gathered once
+// from the slot pool into LDS and shared by all rows -- the prefix is read
+// once for every tree node and head ("The DDTree CUDA Graph Fix ...",
+// section "The DDTree Architecture: Confirming Multiple-Path Evaluation").
 //
-// Per block and wave pair (32 rows x 32 columns):
+// Scores: waves pair up; pair g owns rows 32g .. 32g+31 and wave half h
+// contracts latent features [288h, 288h+288):
 //   partial S^T[32 col x 32 row] = K[32 x 288] . Q^T[288 x 32]   18 x mfma_f32_32x32x16_bf16
 //     A = latent rows from LDS (ds_read_b128), B = the wave's half of the
 //     queries, kept in registers for the whole tile.  With columns as the
 //     MFMA row index each lane's accumulator holds ONE query row, so the
 //     row max is one cross-half exchange and the output rescale is one
-//     multiplier per lane.  The two halves are summed through LDS.
+//     multiplier per lane.  Half 1 hands its partial to half 0 through LDS.
 //   mask: prefix columns always visible; column P + j visible iff bit j of
 //     the row's ancestor bitset is set (tail blocks only).
-//   online softmax in base 2 (identical in both waves); P^T rounded to bf16.
-//   O^T[256 x 32 row] += V^T[256 x 32 col] . P^T                16 x mfma_f32_32x32x16_bf16
+//   online softmax in base 2; P^T rounded to bf16 and published in LDS in
+//     the accumulator's own lane layout (the columns' order inside the k
+//     dimension is permuted to match it), half 0 doing columns 0-7 of each
+//     lane and half 1 columns 8-15.
+// Values: wave w produces output features [128w, 128w+128) for all 64 rows:
+//   O^T[128 x 64 row] += V^T[128 x 32 col] . P^T[32 col x 64 row]   16 x mfma_f32_32x32x16_bf16
 //     A = c_kv columns read transposed from LDS with ds_read_b64_tr_b16,
-//     B = P^T straight from the score accumulator: the columns' order inside
-//     the k dimension is permuted to match the accumulator layout, so P
-//     never moves between lanes.
-// Splitting the pair this way keeps each LDS byte feeding 32 rows while a
-// wave needs only 72 VGPRs of queries and 128 accumulators of output.
+//     each fragment serving both row groups; B = P^T from LDS.
+// Each LDS byte of a block thus feeds 64 rows of values and 32 rows of each
+// score half, while a wave keeps 72 VGPRs of queries and 128 accumulators.
 //
 // Block buffer layout.  A block is 32 latent rows x 72 chunks of 16 bytes,
 // stored as 36 groups of 1 KB: group 2m + h holds chunks 4m .. 4m+3 of rows
 // 16h .. 16h+15, and 16-byte position 4u + v of the group holds chunk
 // 4m + ((v - (u >> 2)) & 3) of row 16h + u.
-// * gather: one global_load_lds_dwordx4 fills one group (lane = position).
-//   Each 4-lane quad reads one 64-byte span of one row (a quarter of the
-//   lanes' cache lines, coalesced), and wave w fetches rows 16 (w & 1) + l/4,
-//   features [288 (w >> 1), +288) of them: one pool address per lane and
-//   block, the 64-byte steps in the instruction's immediate offset.
+// * gather: one buffer_load_dwordx4 ... lds fills one group (lane =
+//   position).  Each 4-lane quad reads one 64-byte span of one row (a
+//   quarter of the lanes' cache lines, coalesced), and wave w fetches rows
+//   16 (w & 1) + l/4, features [288 (w >> 1), +288) of them: one pool offset
+//   per lane and block, the 64-byte steps in the instruction's immediate.
 // * score fragment (k-step j, lane l: row l & 31, chunk 2j + (l >> 5)): two
 //   base addresses (j even / odd) plus an immediate 2 KB * (j >> 1).
 // * transposed value fragments (4 rows x 16 features per 16 lanes): two
@@ -45,11 +45,12 @@
 // rotation by (u >> 2) puts the lanes of each phase of both patterns on 16
 // distinct 16-byte positions mod 256 bytes, so neither has bank conflicts.
 //
-// Pipeline: four block buffers, two blocks in flight.  Iteration b holds the
-// partial scores of block b; it starts the gather of block b+3, completes
-// S(b) with the partner's half and runs its softmax under the 18 score
-// MFMAs of block b+1, then runs the 16 value MFMAs of block b with the rest
-// of the exponentials underneath and hands S(b+1)'s half to the partner.
+// Pipeline: four block buffers, two blocks in flight, two barriers per
+// block.  Iteration b starts the gather of block b+3 and runs the 18 score
+// MFMAs of block b+1 (half 1 weighs its columns of block b underneath),
+// then the 16 value MFMAs of block b (half 0 runs the first part of the
+// softmax of block b+1 underneath).  The loop is compiled once per half so
+// that each wave executes only its own share of the softmax.
 #include "attn_common.h"
 #include "common.h"
 
@@ -69,9 +70,11 @@ constexpr int ROWB = LATENT * 2;   // 1152 bytes per latent row
 constexpr int BUFB = KB * ROWB;    // 36864 bytes per block buffer
 constexpr int LOADS = BUFB / 1024; // 36 one-KB groups per block
 constexpr int NBUF = 4;            // block buffers: two blocks in flight
-constexpr int XCH = 64 * 64;       // bytes per wave of score-exchange space (64 lanes x 16 f32)
+constexpr int XCH = 64 * 64;       // bytes per pair of score-exchange space (64 lanes x 16 f32)
+constexpr int PBYTES = 4 * 1024;   // P^T of a block: 2 row groups x 2 column halves x 1 KB
+constexpr int ABYTES = 64 * 4;     // one rescale factor per tile row
 constexpr int KS_HALF = 18;        // k-steps of 16 features per half of the 576-wide score
-constexpr int FB_HALF = 8;         // 32-feature output blocks per half of the 512 outputs
+constexpr int FB_WAVE = 4;         // 32-feature output blocks per wave (128 of the 512 outputs)
 constexpr float LN2 = 0.693147180559945309f;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14)
@@ -79,15 +82,24 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | 
 constexpr int WAIT_LGKM0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
 
 
+// Workgroup barrier after an explicit wait (an s_waitcnt immediate).  The
+// empty asm statements with a memory clobber keep the compiler from moving
+// any memory access across the barrier (the barrier builtin alone does not
+// order memory for the optimiser); they emit nothing.
+template <int WAITCNT>
+__device__ inline void barrier_after() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(WAITCNT);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroup barrier that waits only for this wave's LDS traffic, leaving the
 // global->LDS gathers of later blocks in flight (__syncthreads() would wait
 // for every outstanding memory operation).
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
+__device__ inline void lds_barrier() { barrier_after<WAIT_LGKM0>(); }
 
 __device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -128,14 +140,25 @@ __device__ inline float other_half(float x) {
   return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
-template <int NW>
+// BUF: the pool is addressed through a buffer resource (32-bit offsets,
+// pools under 4 GiB).  The gathers are then buffer_load ... lds, which the
+// compiler's wait-count tracking keeps apart from LDS reads, so the LDS
+// reads of fragments wait only for themselves.  With global_load_lds (the
+// form for larger pools) every LDS read waits for all outstanding LDS
+// traffic.
+template <int NW, bool BUF>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
+  // The body uses buffer-resource builtins that exist only for the device;
+  // the host pass needs nothing but the kernel's symbol.
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int MT = 16 * NW;
   static_assert(MT == MT_BF16, "tile rows must match the schedule");
   static_assert(NW == 4, "the block layout splits the gather over 2 x 2 waves");
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUFB + NW * XCH];
-  lds_char* lds = (lds_char*)smem;  // generic -> LDS address space
-  lds_char* xch = lds + NBUF * BUFB;
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUFB + 2 * XCH + PBYTES + ABYTES];
+  lds_char* lds = (lds_char*)smem;       // generic -> LDS address space
+  lds_char* xch = lds + NBUF * BUFB;     // score halves: one slot per pair
+  lds_char* pbuf = xch + 2 * XCH;        // P^T fragments of both pairs
+  lds_char* abuf = pbuf + PBYTES;        // rescale factors of both pairs' rows
 
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
@@ -143,8 +166,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
   const int pair = wave >> 1, half = wave & 1;
   const __bf16* __restrict__ qg = static_cast<const __bf16*>(p.q);
   const char* __restrict__ poolb = static_cast<const char*>(p.pool);
-  const int xmine = wave * XCH + lane * 16;
-  const int xpart = (wave ^ 1) * XCH + lane * 16;
+  const __amdgpu_buffer_rsrc_t pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.pool), 0, (int)(unsigned)min((long long)p.num_slots * ROWB, 0xffffffffLL),
+      0x00020000);  // gfx9 raw buffer: untyped, no swizzle
+  const int xofs = pair * XCH + lane * 16;  // the pair's exchange slot, this lane's 16 bytes per KB
+  const int pofs = lane * 16;               // P^T fragment (row group rg, column half k2) at 1 KB (2 rg + k2)
 
   // ---- lane constants of the buffer layout (header comment) ----
   // score fragments: k-step 18 * half + k at kofs[k & 1] + 2048 * (k >> 1)
@@ -156,14 +182,15 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     kofs0 = kb + 16 * ((hl + (u >> 2)) & 3);
     kofs1 = kb + 16 * ((2 + hl + (u >> 2)) & 3);
   }
-  // value fragments of output block fb, column half k2, row quad t at
-  // vofs[t] + 2048 * fb + 1024 * k2: in 16-lane group g, lane c supplies block
-  // row 16 k2 + 8 t + 4 (l >> 5) + (c >> 2), features 16 (g & 1) + 4 (c & 3) .. +3
+  // value fragments of the wave's output block fb, column half k2, row quad t
+  // at vofs[t] + 2048 * fb + 1024 * k2: in 16-lane group g, lane c supplies
+  // block row 16 k2 + 8 t + 4 (l >> 5) + (c >> 2), features
+  // 128 wave + 32 fb + 16 (g & 1) + 4 (c & 3) .. +3
   int vofs0, vofs1;
   {
     const int g16 = lane >> 4, cq = lane & 15;
     const int cp = 2 * (g16 & 1) + ((cq & 3) >> 1);  // chunk inside the group's 4
-    const int vb = 16 * 1024 * half + 64 * (4 * hl + (cq >> 2)) + 8 * (cq & 1);
+    const int vb = 8 * 1024 * wave + 64 * (4 * hl + (cq >> 2)) + 8 * (cq & 1);
     vofs0 = vb + 16 * ((cp + hl) & 3);
     vofs1 = vb + 512 + 16 * ((cp + 2 + hl) & 3);
   }
@@ -274,10 +301,15 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) vw[k] = k < p.W ? vrow[k] : 0u;
 
-    f32x16_t o[FB_HALF];
+    // O^T of the wave's 128 output features for all 64 rows of the tile
+    f32x16_t o[2][FB_WAVE];  // [row group][32-feature block]
 #pragma unroll
-    for (int fb = 0; fb < FB_HALF; ++fb) o[fb] = f32x16_t{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int fb = 0; fb < FB_WAVE; ++fb) o[rg][fb] = f32x16_t{};
+    // softmax reference of the pair's rows (kept by half 0; half 1's copy
+    // is unused)
+    float m_run = -INFINITY;
     const float c = p.scale_log2;
 
     // slot of the block row this lane gathers in block b (a register load,
@@ -294,32 +326,190 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       // wait for the index load) cannot be hoisted to the load itself.
       asm volatile("" : "+v"(sid));
       sid = min(max(sid, 0), nslot_m1);
-      return poolb + (long long)sid * ROWB + gofs;
+      if constexpr (BUF)
+        return (int)((unsigned)sid * ROWB + gofs);  // byte offset in the pool
+      else
+        return poolb + (long long)sid * ROWB + gofs;
     };
-    auto gather_one = [&](lds_char* dst, const char* src, auto ic) {
+    auto gather_one = [&](lds_char* dst, auto src, auto ic) {
       constexpr int i = decltype(ic)::value;
-      __builtin_amdgcn_global_load_lds(
-          src, reinterpret_cast<__attribute__((address_space(3))) void*>(dst + wofs + 1984 * i), 16,
-          64 * i, 0);
+      auto* d = reinterpret_cast<__attribute__((address_space(3))) void*>(dst + wofs + 1984 * i);
+      if constexpr (BUF)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rsrc, d, 16, src, 0, 64 * i, 0);
+      else
+        __builtin_amdgcn_global_load_lds(src, d, 16, 64 * i, 0);
     };
     auto issue_data = [&](lds_char* dst, int sid) {
-      const char* src = gather_src(sid);
+      const auto src = gather_src(sid);
       static_for<0, LOADS / NW>([&](auto ic) { gather_one(dst, src, ic); });
     };
     constexpr int LPW = LOADS / NW;  // gather loads per wave per block
     constexpr int KDEPTH = 4;        // score fragments read ahead
-    constexpr int VDEPTH = 2;        // value MFMAs whose fragments are read ahead
+    constexpr int VDEPTH = 3;        // value fragments read ahead
+
+    // visibility of block blk's 32 columns to this lane's row (bit c =
+    // column blk * KB + c); nothing past the segment is visible
+    auto mask_word = [&](int blk) -> uint32_t {
+      const int cb = blk * KB;
+      const int ncol = g.N - cb;  // columns of the block that exist
+      if (blk >= b_end || ncol <= 0) return 0u;
+      const int jbase = cb - g.P;  // tree index of the block's column 0
+      uint32_t m32;
+      if (jbase >= 0) {
+        const int w0 = jbase >> 5, sh = jbase & 31;
+        uint32_t lo, hi;
+        if (p.W <= 4) {
+          lo = w0 == 0 ? vw[0] : (w0 == 1 ? vw[1] : (w0 == 2 ? vw[2] : vw[3]));
+          hi = w0 == 0 ? vw[1] : (w0 == 1 ? vw[2] : (w0 == 2 ? vw[3] : 0u));
+        } else {  // trees of more than 128 nodes
+          lo = w0 < p.W ? vrow[w0] : 0u;
+          hi = w0 + 1 < p.W ? vrow[w0 + 1] : 0u;
+        }
+        m32 = sh == 0 ? lo : (lo >> sh) | (hi << (32 - sh));
+      } else if (jbase <= -KB) {  // prefix columns only
+        m32 = 0xffffffffu;
+      } else {  // prefix columns 0 .. -jbase-1, then tree nodes 0, 1, ...
+        const int np = -jbase;
+        m32 = (0xffffffffu >> (32 - np)) | (vw[0] << np);
+      }
+      if (ncol < 32) m32 &= (1u << ncol) - 1u;
+      return m32;
+    };
 
     // ------------------------------------------------------------------
-    // Prologue: gather blocks b0 .. b0+2, compute this wave's half of S(b0),
-    // hand it to the partner, and read the first score fragments of b0+1.
+    // Softmax of one block, split between the pair's two waves and cut into
+    // stages that each sit under one MFMA.
+    //   half 0, under the value MFMAs of the previous block: adds the
+    //     partner's half of the scores, masks, takes the block max, moves
+    //     the reference, weighs columns 0-7 (P^T, k-half 0) and hands the
+    //     scaled, shifted scores of columns 8-15 to half 1 through the
+    //     pair's exchange slot; publishes P^T k-half 0 and the rows'
+    //     rescale factor.
+    //   half 1, under the score MFMAs of the next block: weighs columns
+    //     8-15 and publishes P^T k-half 1.
+    // The block loop is compiled once per half, so each wave runs only its
+    // own part.
+    // ------------------------------------------------------------------
+    f32x16_t s;
+    f32x4 xp[4], th[2];
+    float mb = 0.f, mu = 0.f, psum0 = 0.f, psum1 = 0.f, alpha = 1.f;
+    float l0 = 0.f, l1 = 0.f;  // row sums of the lane's columns 0-7 (half 0) and 8-15 (half 1)
+    bf16x8_t pk0, pk1;
+    auto sm_read = [&](const lds_char* xb) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        xp[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(xb + xofs +
+                                                                                 k * 1024);
+    };
+    auto sm_add = [&](const f32x16_t& sp, int q) {  // columns of accumulator quarters 2q, 2q+1
+#pragma unroll
+      for (int k = 2 * q; k < 2 * q + 2; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * k + e] = sp[4 * k + e] + xp[k][e];
+    };
+    auto sm_mask = [&](int blk) {
+      // lane l holds columns 8 (x >> 2) + 4 (l >> 5) + (x & 3)
+      const uint32_t mine = mask_word(blk) >> (4 * hl);
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+        if (!((mine >> (8 * (x >> 2) + (x & 3))) & 1u)) s[x] = -INFINITY;
+    };
+    auto sm_max = [&]() {
+      const float mx0 = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                              fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      const float mx1 = fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                              fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15])));
+      mb = fmaxf(mx0, mx1);
+    };
+    auto sm_ref = [&]() {
+      mb = fmaxf(mb, other_half(mb)) * c;  // c > 0
+      // Online softmax reference in base 2, moved lazily: m_run changes only
+      // when the block max exceeds it by RESCALE_SLACK (log2 units), so the
+      // accumulator rescale is rare and weights stay below 2^RESCALE_SLACK.
+      // O and l share the reference, so the result is exact.
+      constexpr float RESCALE_SLACK = 8.f;
+      const bool move = mb > m_run + RESCALE_SLACK;  // also true while m_run is -inf
+      const float m_new = move ? mb : m_run;
+      // rows that keep their reference get exactly 1 (also when it is still -inf)
+      alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l0 *= alpha;
+      m_run = m_new;
+      mu = m_run == -INFINITY ? 0.f : m_run;  // all columns masked so far
+      psum0 = 0.f;
+    };
+    auto sm_hand = [&](lds_char* xb) {  // half 0 -> half 1: columns 8-15 as exponents
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        f32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = fmaf(s[8 + 4 * k + e], c, -mu);
+        *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xb + xofs + k * 1024) = t;
+      }
+    };
+    auto sm_exp0 = [&](int x) {  // weight of column x (0-7) under the reference
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[x], c, -mu));
+      psum0 += e;
+      pk0[x] = (__bf16)e;
+    };
+    auto sm_publish0 = [&](lds_char* pb, lds_char* ab) {
+      *reinterpret_cast<__attribute__((address_space(3))) bf16x8_t*>(pb + 2 * pair * 1024 + pofs) =
+          pk0;
+      if (hl == 0)
+        reinterpret_cast<__attribute__((address_space(3))) float*>(ab)[pair * 32 + l32] = alpha;
+      l0 += psum0;
+    };
+    auto sm_read1 = [&](const lds_char* xb) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        th[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(xb + xofs +
+                                                                                 k * 1024);
+      psum1 = 0.f;
+    };
+    auto sm_exp1 = [&](int j) {  // weight of column 8 + j
+      const float e = __builtin_amdgcn_exp2f(th[j >> 2][j & 3]);
+      psum1 += e;
+      pk1[j] = (__bf16)e;
+    };
+    auto sm_publish1 = [&](lds_char* pb, float a_own) {
+      *reinterpret_cast<__attribute__((address_space(3))) bf16x8_t*>(
+          pb + (2 * pair + 1) * 1024 + pofs) = pk1;
+      l1 = l1 * a_own + psum1;
+    };
+    auto score_mfmas = [&](const lds_char* kbuf, bf16x8_t* kf, auto&& under) {
+      // S^T partial of one block (this wave's 288 features); under(k) runs
+      // beneath step k
+      const lds_char* kb0 = kbuf + kofs0;
+      const lds_char* kb1 = kbuf + kofs1;
+      f32x16_t acc = f32x16_t{};
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, KS_HALF>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        under(kc);
+        if (k + KDEPTH < KS_HALF)
+          kf[k + KDEPTH] =
+              lds_read_b128(((k + KDEPTH) & 1 ? kb1 : kb0) + 2048 * ((k + KDEPTH) >> 1));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      return acc;
+    };
+    auto hand_off = [&](const f32x16_t& sp, lds_char* xb) {  // half 1 -> half 0
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f32x4 x = {sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
+        *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xb + xofs + k * 1024) = x;
+      }
+    };
+
+    // ------------------------------------------------------------------
+    // Prologue: gather blocks b0 .. b0+2, the scores and softmax of b0
+    // (P(b0) published), and the first score fragments of b0+1.
     // ------------------------------------------------------------------
     __syncthreads();  // the previous segment is done with all buffers
-    f32x16_t s_mine = f32x16_t{};  // this wave's half of the scores of the current block
-    bf16x8_t kpre[KDEPTH];         // first score fragments of the next block
+    bf16x8_t kpre[KDEPTH];  // first score fragments of the next block
 #pragma unroll
     for (int k = 0; k < KDEPTH; ++k) kpre[k] = bf16x8_t{};
-    int idx_cur = 0;               // slot for the gather of block b+3
+    int idx_cur = 0;        // slot for the gather of block b+3
     if (b_begin < b_end) {
       const int b0 = b_begin;
       // The pipeline is straight-line: blocks past the segment's end are
@@ -332,296 +522,252 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       issue_data(lds + (b0 % NBUF) * BUFB, i0);
       issue_data(lds + ((b0 + 1) % NBUF) * BUFB, i1);
       issue_data(lds + ((b0 + 2) % NBUF) * BUFB, i2);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW));  // blocks b0, b0+1 have landed
-      __builtin_amdgcn_s_barrier();
+      barrier_after<waitcnt_vm_lgkm0(LPW)>();  // blocks b0, b0+1 have landed
+      bf16x8_t kf[KS_HALF];
       {
         const lds_char* kb0 = lds + (b0 % NBUF) * BUFB + kofs0;
         const lds_char* kb1 = lds + (b0 % NBUF) * BUFB + kofs1;
-        f32x16_t sp = f32x16_t{};
 #pragma unroll
-        for (int k = 0; k < KS_HALF; ++k)
-          sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              lds_read_b128((k & 1 ? kb1 : kb0) + 2048 * (k >> 1)), qf[k], sp, 0, 0, 0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f32x4 x = {sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
-          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xch + xmine + k * 1024) = x;
-        }
-        s_mine = sp;
+        for (int k = 0; k < KDEPTH; ++k) kf[k] = lds_read_b128((k & 1 ? kb1 : kb0) + 2048 * (k >> 1));
+      }
+      const f32x16_t sp = score_mfmas(lds + (b0 % NBUF) * BUFB, kf, [](auto) {});
+      if (half == 1) hand_off(sp, xch);
+      {
         const lds_char* nb0 = lds + ((b0 + 1) % NBUF) * BUFB + kofs0;
         const lds_char* nb1 = lds + ((b0 + 1) % NBUF) * BUFB + kofs1;
 #pragma unroll
         for (int k = 0; k < KDEPTH; ++k) kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 2048 * (k >> 1));
       }
       lds_barrier();
+      if (half == 0) {
+        sm_read(xch);
+        sm_add(sp, 0);
+        sm_add(sp, 1);
+        sm_mask(b0);
+        sm_max();
+        sm_ref();
+        sm_hand(xch);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) sm_exp0(x);
+        sm_publish0(pbuf, abuf);
+      }
+      lds_barrier();
     }
 
     // ------------------------------------------------------------------
-    // Iteration b.  Entry: blocks b, b+1 resident, b+2 in flight; this
-    // wave's half of S(b) in s_mine, the partner's in the exchange buffer;
-    // the first KDEPTH score fragments of block b+1 in kpre.
-    // Each MFMA below is one scheduling step (sched_barrier on both sides),
-    // with a hand-placed share of the other work underneath it.
+    // Iteration b.  Entry: blocks b, b+1 resident, b+2 in flight; P^T k-half
+    // 0 of block b, the factors that bring O to its reference and half 1's
+    // exponents of block b published; the first KDEPTH score fragments of
+    // block b+1 in kpre.
+    //   phase A: 18 score MFMAs of block b+1 (the gather of block b+3
+    //            spread underneath); half 1 weighs its columns of block b
+    //            and publishes P^T k-half 1; rare rescale of O; half 1 hands
+    //            its half of S(b+1) to half 0.
+    //   phase B: 16 value MFMAs of block b (each value fragment serves both
+    //            row groups; k-half 0 first, so k-half 1's fragments, read
+    //            after the barrier, arrive in time); underneath, half 0's
+    //            part of the softmax of block b+1; first score fragments of
+    //            block b+2.
+    // Each MFMA is one scheduling step (sched_barrier on both sides).
     // ------------------------------------------------------------------
-    // The four buffers an iteration touches are distinct, and the body says
-    // so with restrict pointers: that lets the compiler see that the
-    // transposing reads of block b cannot alias the gather into block b+3, so
-    // it does not wait for that gather before them.
+    // The buffers an iteration touches are distinct, and the body says so
+    // with restrict pointers: that lets the compiler see that the
+    // transposing reads of block b cannot alias the gather into block b+3,
+    // so it does not wait for that gather before them.
     //   dmab: block b+3 (gather target; held block b-1, whose last reader
     //         finished before the previous barrier)
     //   vbuf: block b (values)   kbuf: block b+1 (scores; stale if none)
     //   nbuf: block b+2 (first score fragments of the next iteration)
-    auto body = [&](int b, auto tail_tag, f32x16_t& s_cur, f32x16_t& sp,
-                    lds_char* __restrict__ dmab, const lds_char* __restrict__ vbuf,
-                    const lds_char* __restrict__ kbuf, const lds_char* __restrict__ nbuf,
-                    lds_char* __restrict__ xb) {
-      constexpr bool TAIL = decltype(tail_tag)::value;
-      // 1. gather of block b+3 (past the end: a valid row into a free
-      //    buffer), then the slot of block b+4.  The gather is spread over
-      //    the score MFMAs below so the address unit drains between loads.
-      //    Its address is formed
-      //    before the next index load, so no wait can cover that load.
-      const char* gsrc = gather_src(idx_cur);
+    // The exchange slot, P^T and rescale regions (xb, pb, ab) carry data
+    // between waves and must not be restrict: the compiler would assume no
+    // other wave writes them and reuse values loaded before a barrier.
+    auto body = [&](int b, auto mask_tag, auto half_tag, lds_char* __restrict__ dmab,
+                    const lds_char* __restrict__ vbuf, const lds_char* __restrict__ kbuf,
+                    const lds_char* __restrict__ nbuf, lds_char* xb, lds_char* pb,
+                    lds_char* ab) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      constexpr int H = decltype(half_tag)::value;  // == half
+      // gather of block b+3 (past the end: a valid row into a free buffer),
+      // then the slot of block b+4.  The gather's address is formed before
+      // the next index load, so no wait can cover that load.
+      const auto gsrc = gather_src(idx_cur);
       const int idx_next = load_idx(b + 4);
 
-      bf16x8_t pk0, pk1, vf[2 * FB_HALF];
-      float psum = 0.f, m_use = 0.f, mb = 0.f;
-      bool move = false;
-      f32x16_t s;
+      // ---- phase A ----
+      bf16x8_t pf[2][2];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) pf[rg][0] = lds_read_b128(pb + 2 * rg * 1024 + pofs);
+      const float a0 = reinterpret_cast<const __attribute__((address_space(3))) float*>(ab)[l32];
+      const float a1 = reinterpret_cast<const __attribute__((address_space(3))) float*>(ab)[32 + l32];
+      if constexpr (H == 1) sm_read1(xb);
+      bf16x8_t kf[KS_HALF];
+#pragma unroll
+      for (int k = 0; k < KDEPTH; ++k) kf[k] = kpre[k];
+      const f32x16_t sp = score_mfmas(kbuf, kf, [&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k % 2 == 1 && k / 2 < LPW)
+          gather_one(dmab, gsrc, std::integral_constant<int, k / 2>{});
+        if constexpr (H == 1 && k >= 2 && k < 10) sm_exp1(k - 2);
+        if constexpr (H == 1 && k == 10) sm_publish1(pb, pair == 0 ? a0 : a1);
+      });
+      // rare: some row's reference moved with block b -- bring O along first
+      if (__ballot(a0 != 1.f || a1 != 1.f) != 0) {  // wave-uniform
+        // The accumulators live in AGPRs; pinning them there on both sides
+        // of the multiply keeps the compiler from moving all of them into
+        // VGPRs for the rest of the loop.
+#pragma unroll
+        for (int fb = 0; fb < FB_WAVE; ++fb) {
+          f32x16_t t0 = o[0][fb], t1 = o[1][fb];
+          asm volatile("" : "+a"(t0), "+a"(t1));
+          t0 *= a0;
+          t1 *= a1;
+          asm volatile("" : "+a"(t0), "+a"(t1));
+          o[0][fb] = t0;
+          o[1][fb] = t1;
+        }
+      }
       const lds_char* vb0 = vbuf + vofs0;
       const lds_char* vb1 = vbuf + vofs1;
-      auto vread = [&](int i) {  // value MFMA i: output block i & 7, column half i >> 3
-        const int off = 2048 * (i & 7) + 1024 * (i >> 3);
+      auto vread = [&](int f) {  // value fragment f: output block f & 3, column half f >> 2
+        const int off = 2048 * (f & 3) + 1024 * (f >> 2);
         const bf16x4_t lo = lds_read_tr(vb0 + off);
         const bf16x4_t hi = lds_read_tr(vb1 + off);
         return (bf16x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      auto expo = [&](int x) {  // weight of score x under the current reference
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[x], c, -m_use));
-        psum += e;
-        return e;
-      };
-      {
-        // 2. phase A: the 18 score MFMAs of block b+1.  Underneath: S(b) =
-        //    own half + partner's half, mask, block max, reference check,
-        //    weights of the lane's first 8 columns.
-        f32x4 xp[4];
+      bf16x8_t vf[2 * FB_WAVE];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          xp[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-              xb + xpart + k * 1024);
-        const lds_char* kb0 = kbuf + kofs0;
-        const lds_char* kb1 = kbuf + kofs1;
-        bf16x8_t kf[KS_HALF];
+      for (int f = 0; f < VDEPTH; ++f) vf[f] = vread(f);
+      if constexpr (H == 1) hand_off(sp, xb);
+
+      // block b+2 has landed (only block b+3's gather may still run); S(b+1)'s
+      // half and P^T k-half 1 of block b are visible, and k-half 0 has been
+      // read by everyone
+      barrier_after<waitcnt_vm_lgkm0(LPW)>();
+
+      // ---- phase B ----
+      const lds_char* nb0 = nbuf + kofs0;
+      const lds_char* nb1 = nbuf + kofs1;
+      static_for<0, 4 * FB_WAVE>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int f = i >> 1, rg = i & 1, fb = f & 3, k2 = f >> 2;
+        if constexpr (rg == 0 && f + VDEPTH < 2 * FB_WAVE) vf[f + VDEPTH] = vread(f + VDEPTH);
+        o[rg][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], pf[rg][k2], o[rg][fb], 0, 0, 0);
+        if constexpr (i == 0) {
 #pragma unroll
-        for (int k = 0; k < KDEPTH; ++k) kf[k] = kpre[k];
-        float mx0 = 0.f;
-        sp = f32x16_t{};
+          for (int r = 0; r < 2; ++r) pf[r][1] = lds_read_b128(pb + (2 * r + 1) * 1024 + pofs);
+        }
+        if constexpr (H == 0) {
+          if constexpr (i == 0) sm_read(xb);
+          if constexpr (i == 2) sm_add(sp, 0);
+          if constexpr (i == 3) {
+            sm_add(sp, 1);
+            if constexpr (MASK) sm_mask(b + 1);
+          }
+          if constexpr (i == 4) sm_max();
+          if constexpr (i == 5) sm_ref();
+          if constexpr (i == 6) sm_hand(xb);
+          if constexpr (i >= 7 && i < 11) {
+            sm_exp0(2 * (i - 7));
+            sm_exp0(2 * (i - 7) + 1);
+          }
+          if constexpr (i == 11) sm_publish0(pb, ab);
+        }
+        if constexpr (i >= 4 * FB_WAVE - KDEPTH) {
+          constexpr int k = i - (4 * FB_WAVE - KDEPTH);
+          kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 2048 * (k >> 1));
+        }
         __builtin_amdgcn_sched_barrier(0);
-        static_for<0, KS_HALF>([&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          if constexpr (k % 2 == 1 && k / 2 < LPW)
-            gather_one(dmab, gsrc, std::integral_constant<int, k / 2>{});
-          if (k + KDEPTH < KS_HALF)
-            kf[k + KDEPTH] =
-                lds_read_b128(((k + KDEPTH) & 1 ? kb1 : kb0) + 2048 * ((k + KDEPTH) >> 1));
-          sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], sp, 0, 0, 0);
-          if (k >= 1 && k <= 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[4 * (k - 1) + e] = s_cur[4 * (k - 1) + e] + xp[k - 1][e];
-          }
-          if (TAIL && k == 5) {
-            // mask: one 32-bit word, bit c = column cb + c visible
-            const int cb = b * KB;
-            const int jbase = cb - g.P;  // tree index of the block's column 0
-            uint32_t m32;
-            if (jbase >= 0) {
-              const int w0 = jbase >> 5, sh = jbase & 31;
-              uint32_t lo, hi;
-              if (p.W <= 4) {
-                lo = w0 == 0 ? vw[0] : (w0 == 1 ? vw[1] : (w0 == 2 ? vw[2] : vw[3]));
-                hi = w0 == 0 ? vw[1] : (w0 == 1 ? vw[2] : (w0 == 2 ? vw[3] : 0u));
-              } else {  // trees of more than 128 nodes
-                lo = w0 < p.W ? vrow[w0] : 0u;
-                hi = w0 + 1 < p.W ? vrow[w0 + 1] : 0u;
-              }
-              m32 = sh == 0 ? lo : (lo >> sh) | (hi << (32 - sh));
-            } else {  // prefix columns 0 .. -jbase-1, then tree nodes 0, 1, ...
-              const int np = -jbase;
-              m32 = (0xffffffffu >> (32 - np)) | (vw[0] << np);
-            }
-            const int ncol = g.N - cb;  // columns of the block that exist
-            if (ncol < 32) m32 &= (1u << ncol) - 1u;
-            // lane l holds columns 8 (x >> 2) + 4 (l >> 5) + (x & 3)
-            const uint32_t mine = m32 >> (4 * hl);
-#pragma unroll
-            for (int x = 0; x < 16; ++x)
-              if (!((mine >> (8 * (x >> 2) + (x & 3))) & 1u)) s[x] = -INFINITY;
-          }
-          if (k == 6)
-            mx0 = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                        fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-          if (k == 7) {
-            const float mx1 = fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
-                                    fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15])));
-            mb = fmaxf(mx0, mx1);
-          }
-          if (k == 8) {
-            mb = fmaxf(mb, other_half(mb)) * c;  // c > 0
-            // Online softmax reference in base 2, moved lazily: m_run
-            // changes only when the block max exceeds it by RESCALE_SLACK
-            // (log2 units), so the accumulator rescale is rare and weights
-            // stay below 2^RESCALE_SLACK.  O and l share the reference, so
-            // the result is exact.
-            constexpr float RESCALE_SLACK = 8.f;
-            move = mb > m_run + RESCALE_SLACK;  // also true while m_run is -inf
-            m_use = m_run == -INFINITY ? 0.f : m_run;  // all columns masked so far
-          }
-          if (k >= 9 && k <= 16) {
-            const int x = k - 9;
-            pk0[x] = (__bf16)expo(x);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        });
+      });
 
-        // 3. rare: the reference moves -- rescale O and l, redo the weights
-        if (__ballot(move) != 0) {  // wave-uniform
-          const float m_new = move ? mb : m_run;
-          // rows that keep their reference get exactly 1 (also when it is still -inf)
-          const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-          // The accumulators live in AGPRs; pinning them there on both sides
-          // of the multiply keeps the compiler from moving all 128 of them
-          // into VGPRs for the rest of the loop.
-#pragma unroll
-          for (int fb = 0; fb < FB_HALF; ++fb) {
-            f32x16_t t = o[fb];
-            asm volatile("" : "+a"(t));
-            t *= alpha;
-            asm volatile("" : "+a"(t));
-            o[fb] = t;
-          }
-          m_run = m_new;
-          m_use = m_run == -INFINITY ? 0.f : m_run;
-          psum = 0.f;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) pk0[x] = (__bf16)expo(x);
-        }
-        // first value fragments of block b (resident since two steps ago)
-#pragma unroll
-        for (int i = 0; i < VDEPTH; ++i) vf[i] = vread(i);
-      }
-
-      // 4. block b+2 has landed (only block b+3's gather may still run) and
-      //    everyone has read the exchange buffer before it is rewritten
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-
-      {
-        // 5. phase B: O^T[half] += V^T[half] P^T for block b, column half 0
-        //    first.  Underneath: the weights of the lane's last 8 columns,
-        //    the hand-off of S(b+1)'s half, the first score fragments of b+2.
-        const lds_char* nb0 = nbuf + kofs0;
-        const lds_char* nb1 = nbuf + kofs1;
-#pragma unroll
-        for (int i = 0; i < 2 * FB_HALF; ++i) {
-          if (i + VDEPTH < 2 * FB_HALF) vf[i + VDEPTH] = vread(i + VDEPTH);
-          o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], i < 8 ? pk0 : pk1, o[i & 7], 0,
-                                                              0, 0);
-          if (i < 8) pk1[i] = (__bf16)expo(8 + i);
-          if (i >= 8 && i < 12) {
-            const int k = i - 8;
-            f32x4 x = {sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
-            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xb + xmine + k * 1024) = x;
-          }
-          if (i >= 2 * FB_HALF - KDEPTH) {
-            const int k = i - (2 * FB_HALF - KDEPTH);
-            kpre[k] = lds_read_b128((k & 1 ? nb1 : nb0) + 2048 * (k >> 1));
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        l_run += psum;
-      }
-
-      // 6. the hand-off is visible
+      // P^T k-half 0 and half 1's exponents of block b+1 are visible;
+      // everyone is done with block b and P^T k-half 1 of block b
       lds_barrier();
       idx_cur = idx_next;
     };
-    auto step = [&](int b, auto tail_tag, f32x16_t& s_cur, f32x16_t& sp) {
-      body(b, tail_tag, s_cur, sp, lds + ((b + 3) % NBUF) * BUFB, lds + (b % NBUF) * BUFB,
-           lds + ((b + 1) % NBUF) * BUFB, lds + ((b + 2) % NBUF) * BUFB, xch);
+    auto step = [&](int b, auto mask_tag, auto half_tag) {
+      body(b, mask_tag, half_tag, lds + ((b + 3) % NBUF) * BUFB, lds + (b % NBUF) * BUFB,
+           lds + ((b + 1) % NBUF) * BUFB, lds + ((b + 2) % NBUF) * BUFB, xch, pbuf, abuf);
     };
 
-    // Blocks that lie wholly inside the prefix need no mask.  The prefix
-    // loop is unrolled by two so the two score registers swap roles instead
-    // of being copied every block.
+    // Iterations whose next block lies wholly inside the prefix need no mask;
+    // the others (and the last, whose next block is past the segment) do.
     using NoMask = std::integral_constant<bool, false>;
     using Mask = std::integral_constant<bool, true>;
-    const int b_mask = max(b_begin, min(b_end, g.P / KB));
-    f32x16_t s_alt = f32x16_t{};
-    int b = b_begin;
-    for (; b + 1 < b_mask; b += 2) {
-      step(b, NoMask{}, s_mine, s_alt);
-      step(b + 1, NoMask{}, s_alt, s_mine);
-    }
-    if (b < b_mask) {
-      step(b, NoMask{}, s_mine, s_alt);
-      s_mine = s_alt;
-      ++b;
-    }
-    for (; b < b_end; ++b) {
-      step(b, Mask{}, s_mine, s_alt);
-      s_mine = s_alt;
-    }
+    // The loops are compiled once per half (wave-uniform dispatch).
+    const int b_full = min(b_end, g.P / KB);
+    auto run_blocks = [&](auto half_tag) {
+      int b = b_begin;
+      for (; b + 1 < b_full; ++b) step(b, NoMask{}, half_tag);
+      for (; b < b_end; ++b) step(b, Mask{}, half_tag);
+    };
+    if (half == 0)
+      run_blocks(std::integral_constant<int, 0>{});
+    else
+      run_blocks(std::integral_constant<int, 1>{});
 
-    // ---- write this segment (rows of the pair, features of the half) ----
-    const float l_tot = l_run + other_half(l_run);
-    if (row_ok && (slot >= 0 || b_begin < b_end)) {  // empty split segments still report m=-inf, l=0
-      const size_t orow = (size_t)g.q0 * p.H + rho;
-      const int fo = 256 * half + 4 * hl;
-      if (slot < 0) {
-        const float inv = 1.f / l_tot;
-        __bf16* out = static_cast<__bf16*>(p.out) + orow * DV + fo;
+    // ---- segment statistics of both pairs' rows, then the output ----
+    // m from half 0; the row sum is half 0's columns plus half 1's
+    const float l_mine = half == 0 ? l0 : l1;
+    const float l_tot = l_mine + other_half(l_mine);
+    auto* stat = reinterpret_cast<__attribute__((address_space(3))) float*>(xch);
+    if (hl == 0) {
+      if (half == 0) stat[pair * 32 + l32] = m_run;
+      stat[(1 + half) * MT + pair * 32 + l32] = l_tot;
+    }
+    lds_barrier();
+    const int fo = 128 * wave + 4 * hl;
 #pragma unroll
-        for (int fb = 0; fb < FB_HALF; ++fb) {
+    for (int rg = 0; rg < 2; ++rg) {
+      const int trow = rg * 32 + l32;
+      const int rho_o = t * MT + trow;
+      const float m_row = stat[trow], l_row = stat[MT + trow] + stat[2 * MT + trow];
+      if (rho_o < g.R && (slot >= 0 || b_begin < b_end)) {  // empty split segments report m=-inf, l=0
+        const size_t orow = (size_t)g.q0 * p.H + rho_o;
+        if (slot < 0) {
+          const float inv = 1.f / l_row;
+          __bf16* out = static_cast<__bf16*>(p.out) + orow * DV + fo;
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            bf16x4_t v4;
+          for (int fb = 0; fb < FB_WAVE; ++fb) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[fb][4 * gq + e] * inv);
-            *reinterpret_cast<bf16x4_t*>(out + 32 * fb + 8 * gq) = v4;
+            for (int gq = 0; gq < 4; ++gq) {
+              bf16x4_t v4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[rg][fb][4 * gq + e] * inv);
+              *reinterpret_cast<bf16x4_t*>(out + 32 * fb + 8 * gq) = v4;
+            }
           }
-        }
-        if (half == 0 && hl == 0 && p.lse) p.lse[orow] = (m_run + log2f(l_tot)) * LN2;
-      } else {
-        float* base = p.ws + slot * slot_floats(MT);
-        const int trow = pair * 32 + l32;
-        float* ob = base + (size_t)trow * DV + fo;
+          if (wave == 0 && hl == 0 && p.lse) p.lse[orow] = (m_row + log2f(l_row)) * LN2;
+        } else {
+          float* base = p.ws + slot * slot_floats(MT);
+          float* ob = base + (size_t)trow * DV + fo;
 #pragma unroll
-        for (int fb = 0; fb < FB_HALF; ++fb) {
+          for (int fb = 0; fb < FB_WAVE; ++fb) {
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            float4 v4 = make_float4(o[fb][4 * gq], o[fb][4 * gq + 1], o[fb][4 * gq + 2],
-                                    o[fb][4 * gq + 3]);
-            *reinterpret_cast<float4*>(ob + 32 * fb + 8 * gq) = v4;
+            for (int gq = 0; gq < 4; ++gq) {
+              float4 v4 = make_float4(o[rg][fb][4 * gq], o[rg][fb][4 * gq + 1],
+                                      o[rg][fb][4 * gq + 2], o[rg][fb][4 * gq + 3]);
+              *reinterpret_cast<float4*>(ob + 32 * fb + 8 * gq) = v4;
+            }
           }
-        }
-        if (half == 0 && hl == 0) {
-          base[(size_t)MT * DV + trow] = m_run;
-          base[(size_t)MT * DV + MT + trow] = l_tot;
+          if (wave == 0 && hl == 0) {
+            base[(size_t)MT * DV + trow] = m_row;
+            base[(size_t)MT * DV + MT + trow] = l_row;
+          }
         }
       }
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 }  // namespace
 
 int launch_bf16(const Params& p, int grid, hipStream_t s) {
   constexpr int NW = MT_BF16 / 16;
-  hipLaunchKernelGGL(attn_bf16_kernel<NW>, dim3(grid), dim3(NW * 64), 0, s, p);
+  if (p.num_slots * (long long)ROWB <= 0xffffffffLL)
+    hipLaunchKernelGGL((attn_bf16_kernel<NW, true>), dim3(grid), dim3(NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<NW, false>), dim3(grid), dim3(NW * 64), 0, s, p);
   return check_launch("verify_attn(bf16)");
 }
 
