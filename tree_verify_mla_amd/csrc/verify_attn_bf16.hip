@@ -16,10 +16,9 @@
 //     multiplier per lane.  Half 1 hands its partial to half 0 through LDS.
 //   mask: prefix columns always visible; column P + j visible iff bit j of
 //     the row's ancestor bitset is set (tail blocks only).
-//   online softmax in base 2; P^T rounded to bf16 and published in LDS in
-//     the accumulator's own lane layout (the columns' order inside the k
-//     dimension is permuted to match it), half 0 doing columns 0-7 of each
-//     lane and half 1 columns 8-15.
+//   online softmax in base 2 (by half 0); P^T rounded to bf16 and
+//     published in LDS in the accumulator's own lane layout (the columns'
+//     order inside the k dimension is permuted to match it).
 // Values: wave w produces output features [128w, 128w+128) for all 64 rows:
 //   O^T[128 x 64 row] += V^T[128 x 32 col] . P^T[32 col x 64 row]   16 x mfma_f32_32x32x16_bf16
 //     A = c_kv columns read transposed from LDS with ds_read_b64_tr_b16,
@@ -47,10 +46,9 @@
 //
 // Pipeline: four block buffers, two blocks in flight, two barriers per
 // block.  Iteration b starts the gather of block b+3 and runs the 18 score
-// MFMAs of block b+1 (half 1 weighs its columns of block b underneath),
+// MFMAs of block b+1 (half 0 weighs columns 8-15 of block b underneath),
 // then the 16 value MFMAs of block b (half 0 runs the first part of the
-// softmax of block b+1 underneath).  The loop is compiled once per half so
-// that each wave executes only its own share of the softmax.
+// softmax of block b+1 underneath).  The loop is compiled once per half.
 #include "attn_common.h"
 #include "common.h"
 
@@ -377,23 +375,21 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     };
 
     // ------------------------------------------------------------------
-    // Softmax of one block, split between the pair's two waves and cut into
-    // stages that each sit under one MFMA.
-    //   half 0, under the value MFMAs of the previous block: adds the
-    //     partner's half of the scores, masks, takes the block max, moves
-    //     the reference, weighs columns 0-7 (P^T, k-half 0) and hands the
-    //     scaled, shifted scores of columns 8-15 to half 1 through the
-    //     pair's exchange slot; publishes P^T k-half 0 and the rows'
-    //     rescale factor.
-    //   half 1, under the score MFMAs of the next block: weighs columns
-    //     8-15 and publishes P^T k-half 1.
-    // The block loop is compiled once per half, so each wave runs only its
-    // own part.
+    // Softmax of one block, run by half 0 of each pair in stages that each
+    // sit under one MFMA.
+    //   under the value MFMAs of the previous block: add the partner's half
+    //     of the scores, mask, take the block max, move the reference, weigh
+    //     the lane's columns 0-7 (P^T k-half 0) and publish them with the
+    //     rows' rescale factor; keep columns 8-15 as exponents;
+    //   under the score MFMAs of the next block: weigh columns 8-15 and
+    //     publish P^T k-half 1.
+    // Half 1 only hands its partial scores over; the block loop is compiled
+    // once per half.
     // ------------------------------------------------------------------
     f32x16_t s;
     f32x4 xp[4], th[2];
     float mb = 0.f, mu = 0.f, psum0 = 0.f, psum1 = 0.f, alpha = 1.f;
-    float l0 = 0.f, l1 = 0.f;  // row sums of the lane's columns 0-7 (half 0) and 8-15 (half 1)
+    float l_run = 0.f;  // row sum of the lane's 16 columns (half 0)
     bf16x8_t pk0, pk1;
     auto sm_read = [&](const lds_char* xb) {
 #pragma unroll
@@ -432,19 +428,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       const float m_new = move ? mb : m_run;
       // rows that keep their reference get exactly 1 (also when it is still -inf)
       alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l0 *= alpha;
+      l_run *= alpha;
       m_run = m_new;
       mu = m_run == -INFINITY ? 0.f : m_run;  // all columns masked so far
       psum0 = 0.f;
     };
-    auto sm_hand = [&](lds_char* xb) {  // half 0 -> half 1: columns 8-15 as exponents
+    auto sm_defer = [&]() {  // columns 8-15 as exponents, weighed one phase later
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        f32x4 t;
+      for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = fmaf(s[8 + 4 * k + e], c, -mu);
-        *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(xb + xofs + k * 1024) = t;
-      }
+        for (int e = 0; e < 4; ++e) th[k][e] = fmaf(s[8 + 4 * k + e], c, -mu);
+      psum1 = 0.f;
     };
     auto sm_exp0 = [&](int x) {  // weight of column x (0-7) under the reference
       const float e = __builtin_amdgcn_exp2f(fmaf(s[x], c, -mu));
@@ -456,24 +450,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
           pk0;
       if (hl == 0)
         reinterpret_cast<__attribute__((address_space(3))) float*>(ab)[pair * 32 + l32] = alpha;
-      l0 += psum0;
-    };
-    auto sm_read1 = [&](const lds_char* xb) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        th[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(xb + xofs +
-                                                                                 k * 1024);
-      psum1 = 0.f;
+      l_run += psum0;
     };
     auto sm_exp1 = [&](int j) {  // weight of column 8 + j
       const float e = __builtin_amdgcn_exp2f(th[j >> 2][j & 3]);
       psum1 += e;
       pk1[j] = (__bf16)e;
     };
-    auto sm_publish1 = [&](lds_char* pb, float a_own) {
+    auto sm_publish1 = [&](lds_char* pb) {
       *reinterpret_cast<__attribute__((address_space(3))) bf16x8_t*>(
           pb + (2 * pair + 1) * 1024 + pofs) = pk1;
-      l1 = l1 * a_own + psum1;
+      l_run += psum1;
     };
     auto score_mfmas = [&](const lds_char* kbuf, bf16x8_t* kf, auto&& under) {
       // S^T partial of one block (this wave's 288 features); under(k) runs
@@ -546,7 +533,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         sm_mask(b0);
         sm_max();
         sm_ref();
-        sm_hand(xch);
+        sm_defer();
 #pragma unroll
         for (int x = 0; x < 8; ++x) sm_exp0(x);
         sm_publish0(pbuf, abuf);
@@ -556,11 +543,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
 
     // ------------------------------------------------------------------
     // Iteration b.  Entry: blocks b, b+1 resident, b+2 in flight; P^T k-half
-    // 0 of block b, the factors that bring O to its reference and half 1's
-    // exponents of block b published; the first KDEPTH score fragments of
-    // block b+1 in kpre.
+    // 0 of block b and the factors that bring O to its reference published,
+    // half 0 holding the exponents of columns 8-15 of block b; the first
+    // KDEPTH score fragments of block b+1 in kpre.
     //   phase A: 18 score MFMAs of block b+1 (the gather of block b+3
-    //            spread underneath); half 1 weighs its columns of block b
+    //            spread underneath); half 0 weighs columns 8-15 of block b
     //            and publishes P^T k-half 1; rare rescale of O; half 1 hands
     //            its half of S(b+1) to half 0.
     //   phase B: 16 value MFMAs of block b (each value fragment serves both
@@ -599,7 +586,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       for (int rg = 0; rg < 2; ++rg) pf[rg][0] = lds_read_b128(pb + 2 * rg * 1024 + pofs);
       const float a0 = reinterpret_cast<const __attribute__((address_space(3))) float*>(ab)[l32];
       const float a1 = reinterpret_cast<const __attribute__((address_space(3))) float*>(ab)[32 + l32];
-      if constexpr (H == 1) sm_read1(xb);
       bf16x8_t kf[KS_HALF];
 #pragma unroll
       for (int k = 0; k < KDEPTH; ++k) kf[k] = kpre[k];
@@ -607,8 +593,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k % 2 == 1 && k / 2 < LPW)
           gather_one(dmab, gsrc, std::integral_constant<int, k / 2>{});
-        if constexpr (H == 1 && k >= 2 && k < 10) sm_exp1(k - 2);
-        if constexpr (H == 1 && k == 10) sm_publish1(pb, pair == 0 ? a0 : a1);
+        if constexpr (H == 0 && k >= 2 && k < 10) sm_exp1(k - 2);
+        if constexpr (H == 0 && k == 10) sm_publish1(pb);
       });
       // rare: some row's reference moved with block b -- bring O along first
       if (__ballot(a0 != 1.f || a1 != 1.f) != 0) {  // wave-uniform
@@ -665,7 +651,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
           }
           if constexpr (i == 4) sm_max();
           if constexpr (i == 5) sm_ref();
-          if constexpr (i == 6) sm_hand(xb);
+          if constexpr (i == 6) sm_defer();
           if constexpr (i >= 7 && i < 11) {
             sm_exp0(2 * (i - 7));
             sm_exp0(2 * (i - 7) + 1);
@@ -679,8 +665,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         __builtin_amdgcn_sched_barrier(0);
       });
 
-      // P^T k-half 0 and half 1's exponents of block b+1 are visible;
-      // everyone is done with block b and P^T k-half 1 of block b
+      // P^T k-half 0 of block b+1 is visible; everyone is done with block b
+      // and P^T k-half 1 of block b
       lds_barrier();
       idx_cur = idx_next;
     };
@@ -706,13 +692,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
       run_blocks(std::integral_constant<int, 1>{});
 
     // ---- segment statistics of both pairs' rows, then the output ----
-    // m from half 0; the row sum is half 0's columns plus half 1's
-    const float l_mine = half == 0 ? l0 : l1;
-    const float l_tot = l_mine + other_half(l_mine);
+    // m and l of each pair's rows come from its half 0
+    const float l_tot = l_run + other_half(l_run);
     auto* stat = reinterpret_cast<__attribute__((address_space(3))) float*>(xch);
-    if (hl == 0) {
-      if (half == 0) stat[pair * 32 + l32] = m_run;
-      stat[(1 + half) * MT + pair * 32 + l32] = l_tot;
+    if (half == 0 && hl == 0) {
+      stat[pair * 32 + l32] = m_run;
+      stat[MT + pair * 32 + l32] = l_tot;
     }
     lds_barrier();
     const int fo = 128 * wave + 4 * hl;
@@ -720,7 +705,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
     for (int rg = 0; rg < 2; ++rg) {
       const int trow = rg * 32 + l32;
       const int rho_o = t * MT + trow;
-      const float m_row = stat[trow], l_row = stat[MT + trow] + stat[2 * MT + trow];
+      const float m_row = stat[trow], l_row = stat[MT + trow];
       if (rho_o < g.R && (slot >= 0 || b_begin < b_end)) {  // empty split segments report m=-inf, l=0
         const size_t orow = (size_t)g.q0 * p.H + rho_o;
         if (slot < 0) {
