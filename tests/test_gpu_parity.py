@@ -185,8 +185,11 @@ def test_dense_mask_matches_oracle():
 def test_build_tree_exact_many_shapes():
     """Bit-exact trees over depth/top-k/budget combinations, incl. ties."""
     _say("test_build_tree_exact_many_shapes")
+    # budgets above 126 take the LDS-frontier kernel, the others the register
+    # one; depth x top-k above 256 keeps the top-k table in LDS
     for (D, K, budgets) in [(7, 4, [8, 0, 3]), (7, 8, [32, 16, 64]), (7, 16, [64, 1, 40]),
-                            (3, 2, [14, 7, 1]), (1, 5, [5, 2, 0])]:
+                            (3, 2, [14, 7, 1]), (1, 5, [5, 2, 0]), (7, 8, [126, 125, 2]),
+                            (7, 8, [200, 127, 9]), (7, 40, [100, 12, 3])]:
         wl = make_workload(get_config(3), bs=3, heads=1, depth=D, topk=K, budgets=budgets,
                            prefixes=[4, 4, 4], pool_slots=400, seed=77 + D * K)
         # coarse log-probs give exact fp32 ties in the scores

@@ -16,6 +16,15 @@
 // Order: higher fp32 score first, then smaller depth, then the
 // lexicographically smaller rank path.  Rank paths are packed big-endian in
 // 64 bits (rank_bits per depth), so equal-depth paths compare as integers.
+// Two candidates never share a rank path, so the order is total.
+//
+// Budgets up to 126 run build_tree_reg_kernel: the frontier lives in
+// registers, two entries per lane, and a step is one wave-wide max of a
+// 32-bit score key (DPP inside each 16-lane row, then the four row results
+// in scalar registers), a ballot, and per-lane selects that put the taken
+// entry's best child in its slot and append its sibling.  Exact score ties fall to
+// a rarely taken exact tie-break on depth and rank path.  Larger budgets run
+// build_tree_kernel, which keeps the frontier in LDS.
 #include <climits>
 
 #include "common.h"
@@ -167,6 +176,229 @@ __global__ __launch_bounds__(64) void build_tree_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Register frontier (budget <= REG_MAX_BUDGET)
+// ---------------------------------------------------------------------------
+constexpr int REG_MAX_BUDGET = 126;  // frontier slots <= budget + 1 <= 127 < 2 x 64
+
+// value of lane src_lane (uniform) of x
+__device__ inline uint32_t lane_val(uint32_t x, int src_lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, src_lane);
+}
+
+// wave-wide maximum (MAX) or minimum of x, uniform result
+template <bool MAX>
+__device__ inline uint32_t wave_ext(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  // inside each 16-lane row: swap neighbours, pairs, then mirror halves
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));
+  return op(op(lane_val(x, 0), lane_val(x, 16)), op(lane_val(x, 32), lane_val(x, 48)));
+}
+
+// order-preserving map of an fp32 score to uint32 (larger score -> larger key)
+__device__ inline uint32_t score_key(float f) {
+  const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);  // -0 ties with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One frontier entry.  meta packs depth (7 bits), rank (13 bits) and parent
+// node (11 bits) -- depth_max * rank_bits <= 64, depth_max * topk <= 8192
+// and the budget <= 126 bound them -- plus a valid bit.
+struct Slot {
+  float score, pscore;
+  uint32_t meta, code_lo, code_hi;
+};
+__device__ inline uint32_t pack_meta(int depth, int rank, int parent) {
+  return 0x80000000u | ((uint32_t)parent << 20) | ((uint32_t)rank << 7) | (uint32_t)depth;
+}
+__device__ inline int meta_depth(uint32_t m) { return (int)(m & 0x7f); }
+__device__ inline int meta_rank(uint32_t m) { return (int)((m >> 7) & 0x1fff); }
+__device__ inline int meta_parent(uint32_t m) { return (int)((m >> 20) & 0x7ff); }
+
+__device__ inline Slot bcast(const Slot& x, int lane) {
+  Slot r;
+  r.score = __uint_as_float(lane_val(__float_as_uint(x.score), lane));
+  r.pscore = __uint_as_float(lane_val(__float_as_uint(x.pscore), lane));
+  r.meta = lane_val(x.meta, lane);
+  r.code_lo = lane_val(x.code_lo, lane);
+  r.code_hi = lane_val(x.code_hi, lane);
+  return r;
+}
+
+__device__ inline Slot pick(bool c, const Slot& a, const Slot& b) {
+  Slot r;
+  r.score = c ? a.score : b.score;
+  r.pscore = c ? a.pscore : b.pscore;
+  r.meta = c ? a.meta : b.meta;
+  r.code_lo = c ? a.code_lo : b.code_lo;
+  r.code_hi = c ? a.code_hi : b.code_hi;
+  return r;
+}
+
+// Top-k tables of up to TAB_REGS * 64 entries are also held in registers,
+// entry i in lane i & 63, register i >> 6, and read with readlane (a few
+// cycles instead of an LDS round trip).
+constexpr int TAB_REGS = 4;
+
+template <bool REG_TAB>
+__global__ __launch_bounds__(64) void build_tree_reg_kernel(
+    const float* __restrict__ lp, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ roots, const int32_t* __restrict__ qo, int D, int K,
+    int max_budget, int rank_bits, int32_t* __restrict__ tok, int32_t* __restrict__ par,
+    int32_t* __restrict__ dep, float* __restrict__ sc) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* s_lp = reinterpret_cast<float*>(smem);               // [D * K]
+  int32_t* s_id = reinterpret_cast<int32_t*>(s_lp + D * K);   // [D * K]
+
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int base = qo[r];
+  const int Q = qo[r + 1] - base;
+  if (Q < 1) return;
+  const int B = min(Q - 1, max_budget);
+  if (B > 0) {
+    const float* lpg = lp + (size_t)r * D * K;
+    const int32_t* idg = ids + (size_t)r * D * K;
+    for (int i = lane; i < D * K; i += 64) {
+      s_lp[i] = lpg[i];
+      s_id[i] = idg[i];
+    }
+  }
+  __syncthreads();
+
+  for (int i = B + 1 + lane; i < Q; i += 64) {  // budget beyond max_budget
+    tok[base + i] = -1;
+    par[base + i] = -1;
+    dep[base + i] = -1;
+    if (sc) sc[base + i] = 0.f;
+  }
+  if (lane == 0) {
+    tok[base] = roots[r];
+    par[base] = -1;
+    dep[base] = 0;
+    if (sc) sc[base] = 0.f;
+  }
+  if (B <= 0) return;
+
+  // Entry e lives in lane e & 63, slot e >> 6.  A taken entry's slot is
+  // reused by its best child; its sibling is appended at n, so n <= k + 1.
+  // A slot whose entry left no successor stays invalid (meta 0).
+  Slot f[2];
+  // entry i of the tables (uniform i); named registers, not an array, so
+  // that the uniform selection stays in registers
+  uint32_t lp0 = 0, lp1 = 0, lp2 = 0, lp3 = 0, id0 = 0, id1 = 0, id2 = 0, id3 = 0;
+  static_assert(TAB_REGS == 4, "four table registers per lane");
+  if constexpr (REG_TAB) {
+    auto ld = [&](int j, uint32_t& l, uint32_t& t) {
+      const int i = lane + 64 * j;
+      l = i < D * K ? __float_as_uint(s_lp[i]) : 0u;
+      t = i < D * K ? (uint32_t)s_id[i] : 0u;
+    };
+    ld(0, lp0, id0);
+    ld(1, lp1, id1);
+    ld(2, lp2, id2);
+    ld(3, lp3, id3);
+  }
+  auto table = [&](uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3, int i) {
+    const int j = i >> 6;  // uniform
+    const uint32_t v = j == 0 ? t0 : (j == 1 ? t1 : (j == 2 ? t2 : t3));
+    return lane_val(v, i & 63);
+  };
+  auto lp_at = [&](int i) {
+    if constexpr (REG_TAB) return __uint_as_float(table(lp0, lp1, lp2, lp3, i));
+    else return s_lp[i];
+  };
+  auto id_at = [&](int i) {
+    if constexpr (REG_TAB) return (int32_t)table(id0, id1, id2, id3, i);
+    else return s_id[i];
+  };
+
+  const Slot none{0.f, 0.f, 0u, 0u, 0u};
+  f[0] = none;
+  f[1] = none;
+  if (lane == 0) {  // the root's best child
+    f[0].score = __fadd_rn(0.f, s_lp[0]);
+    f[0].meta = pack_meta(1, 0, 0);
+  }
+  int n = 1;
+  for (int k = 1; k <= B; ++k) {
+    // 1. the best entry: largest score key, ties resolved exactly
+    uint32_t key[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t kq = score_key(f[q].score);
+      key[q] = f[q].meta ? kq : 0u;
+    }
+    const uint32_t kmax = wave_ext<true>(max(key[0], key[1]));
+    if (kmax == 0u) {  // empty frontier: only reachable if preconditions are broken
+      for (int i = k + lane; i <= B; i += 64) {
+        tok[base + i] = -1;
+        par[base + i] = -1;
+        dep[base + i] = -1;
+        if (sc) sc[base + i] = 0.f;
+      }
+      break;
+    }
+    uint64_t hit0 = __ballot(key[0] == kmax);
+    uint64_t hit1 = __ballot(key[1] == kmax);
+    if (__popcll(hit0) + __popcll(hit1) > 1) {  // rare: equal scores
+      bool t0 = (hit0 >> lane) & 1, t1 = (hit1 >> lane) & 1;
+      const uint32_t d0 = f[0].meta & 0x7f, d1 = f[1].meta & 0x7f;
+      const uint32_t dmin = wave_ext<false>(min(t0 ? d0 : ~0u, t1 ? d1 : ~0u));
+      t0 = t0 && d0 == dmin;
+      t1 = t1 && d1 == dmin;
+      const uint32_t hmin = wave_ext<false>(min(t0 ? f[0].code_hi : ~0u, t1 ? f[1].code_hi : ~0u));
+      t0 = t0 && f[0].code_hi == hmin;
+      t1 = t1 && f[1].code_hi == hmin;
+      const uint32_t lmin = wave_ext<false>(min(t0 ? f[0].code_lo : ~0u, t1 ? f[1].code_lo : ~0u));
+      t0 = t0 && f[0].code_lo == lmin;
+      t1 = t1 && f[1].code_lo == lmin;
+      hit0 = __ballot(t0);
+      hit1 = __ballot(t1);
+    }
+    const int e = hit0 ? __ffsll((unsigned long long)hit0) - 1
+                       : 64 + __ffsll((unsigned long long)hit1) - 1;
+    const Slot w = bcast(e < 64 ? f[0] : f[1], e & 63);
+    const int d = meta_depth(w.meta), rk = meta_rank(w.meta), p = meta_parent(w.meta);
+
+    // 2. the three table values this step needs, read together (clamped
+    //    indices; a value is used only when its candidate exists)
+    const bool has_child = d < D, has_sib = rk + 1 < K;
+    const int32_t t_id = id_at((d - 1) * K + rk);
+    const float lp_child = lp_at(min(d, D - 1) * K);
+    const float lp_sib = lp_at((d - 1) * K + min(rk + 1, K - 1));
+
+    // 3. the new node
+    if (lane == 0) {
+      tok[base + k] = t_id;
+      par[base + k] = p;
+      dep[base + k] = d;
+      if (sc) sc[base + k] = w.score;
+    }
+
+    // 4. successors: the best child takes slot e, the sibling slot n (or e)
+    const uint64_t code = ((uint64_t)w.code_hi << 32) | w.code_lo;
+    const uint64_t cc = code << rank_bits, cs = code + 1;
+    const Slot child{__fadd_rn(w.score, lp_child), w.score, pack_meta(d + 1, 0, k),
+                     (uint32_t)cc, (uint32_t)(cc >> 32)};
+    const Slot sib{__fadd_rn(w.pscore, lp_sib), w.pscore, pack_meta(d, rk + 1, p), (uint32_t)cs,
+                   (uint32_t)(cs >> 32)};
+    const Slot at_e = has_child ? child : (has_sib ? sib : none);
+    const int pos_sib = has_child && has_sib ? n : -1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = lane + 64 * q;
+      f[q] = pick(idx == e, at_e, f[q]);
+      f[q] = pick(idx == pos_sib, sib, f[q]);
+    }
+    n += pos_sib >= 0 ? 1 : 0;
+  }
+}
+
 }  // namespace
 
 extern "C" int ddtree_build_tree(const float* topk_logprobs, const int32_t* topk_ids,
@@ -205,9 +437,23 @@ extern "C" int ddtree_build_tree(const float* topk_logprobs, const int32_t* topk
                  "build_tree: depth_max * topk = %lld above the supported 8192",
                  (long long)depth_max * topk);
   const size_t staged = max_budget > 0 ? (size_t)depth_max * topk * 8 : 0;  // log-probs + ids
-  const size_t lds = (size_t)(max_budget + 2) * (8 + 4 * 5) + staged;
-  hipLaunchKernelGGL(build_tree_kernel, dim3(bs), dim3(64), lds, ddtree::as_stream(stream),
-                     topk_logprobs, topk_ids, root_tokens, qo_indptr, depth_max, topk, max_budget,
-                     rank_bits, node_tokens, node_parents, node_depths, node_scores);
+  if (max_budget <= REG_MAX_BUDGET) {
+    if ((long long)depth_max * topk <= TAB_REGS * 64)
+      hipLaunchKernelGGL(build_tree_reg_kernel<true>, dim3(bs), dim3(64), staged,
+                         ddtree::as_stream(stream), topk_logprobs, topk_ids, root_tokens, qo_indptr,
+                         depth_max, topk, max_budget, rank_bits, node_tokens, node_parents,
+                         node_depths, node_scores);
+    else
+      hipLaunchKernelGGL(build_tree_reg_kernel<false>, dim3(bs), dim3(64), staged,
+                         ddtree::as_stream(stream), topk_logprobs, topk_ids, root_tokens, qo_indptr,
+                         depth_max, topk, max_budget, rank_bits, node_tokens, node_parents,
+                         node_depths, node_scores);
+  } else {
+    const size_t lds = (size_t)(max_budget + 2) * (8 + 4 * 5) + staged;
+    hipLaunchKernelGGL(build_tree_kernel, dim3(bs), dim3(64), lds, ddtree::as_stream(stream),
+                       topk_logprobs, topk_ids, root_tokens, qo_indptr, depth_max, topk,
+                       max_budget, rank_bits, node_tokens, node_parents, node_depths,
+                       node_scores);
+  }
   return ddtree::check_launch("build_tree");
 }
