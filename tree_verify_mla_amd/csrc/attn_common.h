@@ -31,7 +31,7 @@ constexpr int LATENT = 576;
 constexpr int DV = 512;
 constexpr int KB = 32;          // KV columns per work unit
 constexpr int MIN_UNITS = 8;    // smallest persistent range per workgroup
-constexpr int MT_BF16 = 64;     // rows per tile, bf16 matrix-core kernel (4 waves: 2 pairs x 2 halves)
+constexpr int MT_BF16 = 128;    // rows per tile, bf16 matrix-core kernel (4 waves x 32 rows)
 constexpr int MT_F32 = 4;       // rows per tile, fp32 kernel
 
 struct Params {
