@@ -35,12 +35,18 @@ def hipcc() -> str:
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-result"]
 DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast"]
+# Per-source options.  The matrix-core attention kernel keeps its output
+# accumulators in AGPRs through inline asm and needs the builtin (score) MFMAs
+# in their VGPR-accumulator form, which the compiler would otherwise not pick
+# in a kernel that uses AGPRs.
+SOURCE_FLAGS = {"verify_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: Path, verbose: bool) -> Path:
     obj = BUILD / (src.name + ".o")
     # every source (the .cpp host files too) goes through the HIP language mode
-    cmd = [hipcc(), "-x", "hip", *COMMON, "-c", str(src), "-o", str(obj), *DEVICE_ONLY]
+    cmd = [hipcc(), "-x", "hip", *COMMON, "-c", str(src), "-o", str(obj), *DEVICE_ONLY,
+           *SOURCE_FLAGS.get(src.name, [])]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,6 +58,17 @@ def _compile(src: Path, verbose: bool) -> Path:
     if verbose and msgs:
         print(msgs, flush=True)
     return obj
+
+
+def device_asm(src_name: str, out: Path) -> Path:
+    """gfx950 assembly of one source, compiled with the library's options."""
+    src = CSRC / src_name
+    cmd = [hipcc(), "-x", "hip", *COMMON, "--cuda-device-only", "-S", str(src), "-o", str(out),
+           *DEVICE_ONLY, *SOURCE_FLAGS.get(src_name, [])]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"assembly of {src_name} failed:\n{res.stdout}{res.stderr}")
+    return out
 
 
 def build(verbose: bool = False) -> Path:

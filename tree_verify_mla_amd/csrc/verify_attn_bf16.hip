@@ -150,29 +150,23 @@ __device__ inline bf16x4_t lds_read_tr(const lds_char* p) {
   return __builtin_bit_cast(bf16x4_t, v);
 }
 
-// Register files.  The 256 output accumulators fill the AGPRs (the value
-// MFMAs are builtins; an empty asm that takes them as "a" operands keeps
-// them there where VALU code touches them).  The score accumulator, which the
-// softmax reads, lives in VGPRs with the queries and everything else; since
-// the compiler gives every builtin MFMA an AGPR accumulator in a kernel that
-// may use AGPRs, the score MFMAs are issued as inline asm.  Their hazards
-// (CDNA3/CDNA4 ISA, MFMA dependency rules) are covered here:
-//  * back-to-back accumulation into the same registers needs no wait;
-//  * a VALU write of an operand needs 2 wait states before the MFMA reads it
-//    (s_nop 1 in front; free while the previous MFMA still occupies the
-//    matrix core);
-//  * a VALU access to the result of an 8-pass MFMA needs 11 wait states
-//    (score_done, tied to the accumulator so nothing reads it earlier).
-// Fragment registers loaded from LDS or memory are covered by the compiler's
-// wait counts, which see inline-asm operands.
+// Register files.  The 256 output accumulators fill the AGPRs; the score
+// accumulator, which the softmax reads, lives in VGPRs with the queries and
+// everything else.  The score MFMAs are builtins compiled in VGPR form
+// (-mllvm -amdgpu-mfma-vgpr-form), so the compiler sees them and pads every
+// hazard around them, copies included.  The value MFMAs are inline asm on
+// AGPR operands ("a"): only the next value MFMA on the same accumulator reads
+// their result (back-to-back accumulation needs no wait), and code that
+// touches the accumulators otherwise -- the rare rescale and the epilogue --
+// first waits out the result hazard of an 8-pass MFMA (value_drain), and the
+// rescale leaves 2+ wait states before the next MFMA reads what it wrote.
+// Their A and B operands come straight from LDS reads, covered by the
+// compiler's wait counts (which see inline-asm operands).
+__device__ inline void value_mfma(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void value_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 __device__ inline void in_agprs(f32x16_t& x) { asm volatile("" : "+a"(x)); }
-__device__ inline void score_first(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ inline void score_step(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ inline void score_done(f32x16_t& acc) { asm volatile("s_nop 7\n\ts_nop 4" : "+v"(acc)); }
 // The softmax's arithmetic is pure as well: an empty asm that takes a
 // stage's result keeps the stage under the MFMA it was placed beneath.
 template <typename T>
@@ -495,13 +489,10 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
         under(kc);
         if constexpr (k + KDEPTH < KS)
           kf[k + KDEPTH] = lds_ld<bf16x8_t>(((k + KDEPTH) & 1 ? kb1 : kb0) + 2048 * ((k + KDEPTH) >> 1));
-        if constexpr (k == 0)
-          score_first(acc, kf[k], qf[k]);
-        else
-          score_step(acc, kf[k], qf[k]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], k == 0 ? f32x16_t{} : acc, 0, 0, 0);
+        here(acc);  // keeps the (pure) MFMA at its step
         __builtin_amdgcn_sched_barrier(0);
       });
-      score_done(acc);
       return acc;
     };
     auto kprefetch = [&](const lds_char* kbuf, bf16x8_t* kf) {
@@ -621,6 +612,7 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
 
       // rare: some row's reference moved with block b -- bring O along first
       if (__ballot(af[0] != 1.f || af[1] != 1.f || af[2] != 1.f || af[3] != 1.f) != 0) {
+        value_drain();
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
@@ -631,6 +623,7 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
             in_agprs(x);
             o[rg][fb] = x;
           }
+        asm volatile("s_nop 4" ::: "memory");
       }
 
       // ---- phase B: values of block b, softmax of block b+1 ----
@@ -647,8 +640,7 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
           if constexpr (nf < 2 * FB) vf[nf / FB][nf % FB] = vread(nf % FB, nf / FB);
         }
         if constexpr (k2 == 0 && fb == 2) pf[1][rg] = pread(rg, 1);
-        o[rg][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[k2][fb], pf[k2][rg], o[rg][fb], 0, 0, 0);
-        in_agprs(o[rg][fb]);
+        value_mfma(o[rg][fb], vf[k2][fb], pf[k2][rg]);
         if constexpr (i == 0 && MASK) sm_mask(sn, b + 1);
         if constexpr (i == 1) sm_max0(sn);
         if constexpr (i == 2) sm_max1(sn);
@@ -663,6 +655,9 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
       pc0 = pn0;
       pc1 = pn1;
       idx_cur = idx_next;
+      // the accumulators leave the iteration settled: whatever the compiler
+      // places between iterations (or after the loop) may touch them
+      value_drain();
     };
     auto step = [&](int b, auto mask_tag) {
       body(b, mask_tag, lds + ((b + 3) & (NBUF - 1)) * BUFB, lds + (b & (NBUF - 1)) * BUFB,
@@ -680,6 +675,7 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
       for (; b < b_end; ++b) step(b, Mask{});
     }
 
+    value_drain();
     // ---- segment statistics of every row, then the output ----
     // the own rows' m and l for everyone (lane l32's row of row group wave)
     const float l_own = l_run + other_half(l_run);
