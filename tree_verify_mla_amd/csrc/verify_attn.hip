@@ -96,13 +96,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Params p) {
   }
 }
 
-// Merge of a tile's partial slots: one workgroup per (tile, MERGE_ROWS-row
-// group), wave w owning row w of the group for the statistics.  The slot
-// list and the per-segment weights 2^(m_s - M) are computed once per
-// segment and kept in LDS; the weighted sum of the partial outputs is then
-// a streaming pass (consecutive threads read consecutive float4s of a row).
-constexpr int MERGE_ROWS = 4;    // rows per merge workgroup (= waves)
-constexpr int MERGE_CHUNK = 512; // segments staged in LDS at a time
+// Merge of a tile's partial slots: one wavefront per output row (4 rows per
+// workgroup).  Lane l owns features 8l .. 8l+7 of the row.  The segments are
+// taken MERGE_BATCH at a time: their m, l and partial-output loads are all
+// issued before any is used, then folded in segment order by an online
+// log-sum-exp (the order is fixed, so the result does not depend on timing).
+// Rows are read and written as whole contiguous runs (2 KB of fp32 in, 1 KB
+// of bf16 or 2 KB of fp32 out per row and segment).
+constexpr int MERGE_ROWS = 4;   // rows per merge workgroup (= waves)
+constexpr int MERGE_BATCH = 4;  // segments whose loads are in flight together
 
 // workspace slot of segment k of tile t of request r
 __device__ inline long long merge_slot(const Params& p, long long k, long long first_slot,
@@ -115,14 +117,13 @@ __device__ inline long long merge_slot(const Params& p, long long k, long long f
 
 __global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt, int G, int dtype) {
   const int groups = (mt + MERGE_ROWS - 1) / MERGE_ROWS;
-  const int tile = blockIdx.x / groups, rg = blockIdx.x % groups;
+  const int tile = blockIdx.x / groups, rgrp = blockIdx.x % groups;
   const int r = tile / p.T_max, t = tile % p.T_max;
   if (r >= p.bs) return;
   const Geom g = geom(p.qo, p.kvp, r, p.H, mt);
   if (t >= g.T) return;
-  const int row0 = rg * MERGE_ROWS;                 // first row of the group inside the tile
-  const int rows = min(MERGE_ROWS, g.R - t * mt - row0);
-  if (rows <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = rgrp * MERGE_ROWS + wave;  // row inside the tile
   long long first_slot = 0, w_first = 0, tile_start = 0, U = 0, Ge = 1;
   long long nseg;
   if (p.S > 0) {
@@ -138,85 +139,52 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt
     if (w_first == w_last) return;  // one workgroup covered the tile and wrote it
     nseg = w_last - w_first + 1;
   }
+  if (t * mt + row >= g.R) return;  // after the wave-cooperative sums above
   const long long sf = slot_floats(mt);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-  __shared__ long long s_slot[MERGE_CHUNK];
-  __shared__ float s_w[MERGE_CHUNK][MERGE_ROWS];
-  __shared__ float s_M[MERGE_ROWS], s_L[MERGE_ROWS];
-
-  // pass 1: running max of each row over all segments (wave = row)
-  if (wave < rows) {
-    float M = -INFINITY;
-    for (long long k = lane; k < nseg; k += 64) {
-      const long long slot = merge_slot(p, k, first_slot, w_first, tile_start, U, Ge);
-      M = fmaxf(M, p.ws[slot * sf + (long long)mt * DV + row0 + wave]);
-    }
+  float M = -INFINITY, L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (long long k0 = 0; k0 < nseg; k0 += MERGE_BATCH) {
+    float ms[MERGE_BATCH], ls[MERGE_BATCH];
+    float4 x0[MERGE_BATCH], x1[MERGE_BATCH];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if (lane == 0) s_M[wave] = M;
-  }
-  __syncthreads();
-
-  // pass 2: weights and weighted sums, MERGE_CHUNK segments at a time
-  const int row = tid / (DV / 4 / 2);  // 64 threads x 2 float4 = one row of 512
-  const int f4 = (tid % (DV / 4 / 2)) * 4;  // first of this thread's two float4s: f4, f4 + 256
-  float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
-  float lsum = 0.f;
-  for (long long k0 = 0; k0 < nseg; k0 += MERGE_CHUNK) {
-    const int cnt = (int)min((long long)MERGE_CHUNK, nseg - k0);
-    for (int k = tid; k < cnt; k += blockDim.x)
-      s_slot[k] = merge_slot(p, k0 + k, first_slot, w_first, tile_start, U, Ge);
-    __syncthreads();
-    if (wave < rows) {
-      const float M = s_M[wave];
-      for (int k = lane; k < cnt; k += 64) {
-        const float* base = p.ws + s_slot[k] * sf + (long long)mt * DV;
-        const float ms = base[row0 + wave];
-        const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        s_w[k][wave] = wgt;
-        lsum = fmaf(wgt, base[mt + row0 + wave], lsum);
+    for (int j = 0; j < MERGE_BATCH; ++j) {
+      if (k0 + j < nseg) {
+        const float* base = p.ws + merge_slot(p, k0 + j, first_slot, w_first, tile_start, U, Ge) * sf;
+        ms[j] = base[(long long)mt * DV + row];
+        ls[j] = base[(long long)mt * DV + mt + row];
+        const float4* o = reinterpret_cast<const float4*>(base + (long long)row * DV + 8 * lane);
+        x0[j] = o[0];
+        x1[j] = o[1];
       }
     }
-    __syncthreads();
-    if (row < rows) {
-      for (int k = 0; k < cnt; ++k) {
-        const float wgt = s_w[k][row];
-        const float* o = p.ws + s_slot[k] * sf + (long long)(row0 + row) * DV;
-        const float4 a = *reinterpret_cast<const float4*>(o + f4);
-        const float4 b = *reinterpret_cast<const float4*>(o + f4 + DV / 2);
-        acc0.x = fmaf(wgt, a.x, acc0.x); acc0.y = fmaf(wgt, a.y, acc0.y);
-        acc0.z = fmaf(wgt, a.z, acc0.z); acc0.w = fmaf(wgt, a.w, acc0.w);
-        acc1.x = fmaf(wgt, b.x, acc1.x); acc1.y = fmaf(wgt, b.y, acc1.y);
-        acc1.z = fmaf(wgt, b.z, acc1.z); acc1.w = fmaf(wgt, b.w, acc1.w);
-      }
-    }
-    __syncthreads();  // s_slot / s_w are rewritten by the next chunk
-  }
-  if (wave < rows) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
-    if (lane == 0) s_L[wave] = lsum;
+    for (int j = 0; j < MERGE_BATCH; ++j) {
+      if (k0 + j >= nseg || ms[j] == -INFINITY) continue;  // a segment that saw no column
+      const float Mn = fmaxf(M, ms[j]);
+      const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
+      const float b = exp2f(ms[j] - Mn);
+      const float y[8] = {x0[j].x, x0[j].y, x0[j].z, x0[j].w, x1[j].x, x1[j].y, x1[j].z, x1[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a + y[e] * b;
+      L = L * a + ls[j] * b;
+      M = Mn;
+    }
   }
-  __syncthreads();
-  if (row >= rows) return;
-  const float L = s_L[row], inv = 1.f / L;
-  const size_t orow = (size_t)g.q0 * p.H + (size_t)t * mt + row0 + row;
-  const float o8[8] = {acc0.x * inv, acc0.y * inv, acc0.z * inv, acc0.w * inv,
-                       acc1.x * inv, acc1.y * inv, acc1.z * inv, acc1.w * inv};
+  const float inv = 1.f / L;
+  const size_t orow = (size_t)g.q0 * p.H + (size_t)t * mt + row;
   if (dtype == DDTREE_BF16) {
-    __bf16* out = static_cast<__bf16*>(p.out) + orow * DV;
+    typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+    bf16x8 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      out[f4 + e] = (__bf16)o8[e];
-      out[f4 + DV / 2 + e] = (__bf16)o8[4 + e];
-    }
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + orow * DV + 8 * lane) = v;
   } else {
-    float* out = static_cast<float*>(p.out) + orow * DV;
-    *reinterpret_cast<float4*>(out + f4) = make_float4(o8[0], o8[1], o8[2], o8[3]);
-    *reinterpret_cast<float4*>(out + f4 + DV / 2) = make_float4(o8[4], o8[5], o8[6], o8[7]);
+    float4* out = reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow * DV + 8 * lane);
+    out[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    out[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   }
-  if (f4 == 0 && p.lse) p.lse[orow] = (s_M[row] + log2f(L)) * LN2;
+  if (lane == 0 && p.lse) p.lse[orow] = (M + log2f(L)) * LN2;
 }
 
 }  // namespace
