@@ -330,29 +330,40 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
     ++seg_no;
 
     // ---- this wave's own 32 query rows ----
+    // Loads are issued in the order their results are needed, since a wave's
+    // loads complete in order: the row's ancestor bitset words and the slots
+    // of the first blocks, then the queries, which the gathers need not wait
+    // for.
     const int rho = t * MT + wave * 32 + l32;
     const bool row_ok = rho < g.R;
-    // A wave whose rows all lie past the tile's end still runs the whole
-    // pipeline (on zero queries) so that every wave follows one straight-line
-    // path; the epilogue writes only rows < R.
+    // A row past the tile's end (a wave may hold only such rows) still runs
+    // the whole pipeline, on the queries of the request's row 0, so that every
+    // wave follows one straight-line path; the epilogue writes only rows < R.
     const int node = row_ok ? rho / p.H : g.Q - 1;
-    bf16x8_t qf[KS];  // B operand of k-step j: features 16 j + 8 hl .. +7 of row l32
-    {
-      const __bf16* qrow = qg + ((size_t)g.q0 * p.H + (row_ok ? rho : 0)) * LATENT + 8 * hl;
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k);
-        if (!row_ok) x = bf16x8_t{};
-        qf[k] = x;
-      }
-    }
     // The row's ancestor bitset words, read once per segment: a global load
     // inside the block loop would have to wait behind the in-flight gathers.
-    // Rows of up to 128 tree nodes keep all words in registers.
+    // Rows of up to 128 tree nodes keep all words in registers; words past
+    // the row's W (repeats of its last word) only ever reach columns past the
+    // tree, which the mask clears by position.  No load here is conditional:
+    // the compiler's wait counting through branches would wait for all of
+    // them at once.
+    long long qoff = ((long long)g.q0 * p.H + (row_ok ? rho : 0)) * LATENT + 8 * hl;
+    asm volatile("" : "+v"(qoff));  // address formed before the loads are issued
+    const __bf16* qrow = qg + qoff;
     const uint32_t* vrow = p.vis + (size_t)(g.q0 + node) * p.W;
     uint32_t vw[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) vw[k] = k < p.W ? vrow[k] : 0u;
+    for (int k = 0; k < 4; ++k) vw[k] = vrow[min(k, p.W - 1)];
+    // slot of the block row this lane gathers in block b (clamped to the
+    // request's last column: blocks past the end gather a valid row)
+    const int32_t* kvi = p.kvi + g.kv0;
+    auto load_idx = [&](int b) { return kvi[min(b * KB + grow, g.N - 1)]; };
+    int idx_pro[4];  // slots of blocks b_begin .. b_begin+3
+#pragma unroll
+    for (int k = 0; k < 4; ++k) idx_pro[k] = load_idx(b_begin + k);
+    bf16x8_t qf[KS];  // B operand of k-step j: features 16 j + 8 hl .. +7 of row l32
+#pragma unroll
+    for (int k = 0; k < KS; ++k) qf[k] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k);
 
     f32x16_t o[RG][FB];  // O^T: row group rg, features 128 wave + 32 fb .. +31
 #pragma unroll
@@ -363,9 +374,6 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
         in_agprs(o[rg][fb]);
       }
 
-    // slot of the block row this lane gathers in block b
-    const int32_t* kvi = p.kvi + g.kv0;
-    auto load_idx = [&](int b) { return kvi[min(b * KB + grow, g.N - 1)]; };
     auto gather_src = [&](int sid) {
       // The index is opaque here so that the clamp below (and with it the
       // wait for the index load) cannot be hoisted to the load itself.
@@ -505,7 +513,9 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
     // Prologue: gather blocks b0 .. b0+2, the scores and softmax of b0
     // (P^T(b0) of the own rows), and the first score fragments of b0+1.
     // ------------------------------------------------------------------
-    __syncthreads();  // the previous segment is done with all of LDS
+    // the previous segment is done with all of LDS (its output stores and
+    // this segment's loads above may still be in flight)
+    barrier_after<waitcnt_imm(VM_ANY, 0)>();
     bf16x8_t kpre[KDEPTH];  // first score fragments of the next block
 #pragma unroll
     for (int k = 0; k < KDEPTH; ++k) kpre[k] = bf16x8_t{};
@@ -516,14 +526,11 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
       // The pipeline is straight-line: blocks past the segment's end are
       // "gathered" too (a valid row, into a buffer nobody reads), so every
       // wait below is one fixed count.
-      const int i0 = load_idx(b0);
-      const int i1 = load_idx(b0 + 1);
-      const int i2 = load_idx(b0 + 2);
-      issue_data(lds + (b0 & (NBUF - 1)) * BUFB, i0);
-      issue_data(lds + ((b0 + 1) & (NBUF - 1)) * BUFB, i1);
-      idx_cur = load_idx(b0 + 3);
-      issue_data(lds + ((b0 + 2) & (NBUF - 1)) * BUFB, i2);
-      barrier_after<waitcnt_imm(LPW + 1, 0)>();  // blocks b0, b0+1 have landed
+      issue_data(lds + (b0 & (NBUF - 1)) * BUFB, idx_pro[0]);
+      issue_data(lds + ((b0 + 1) & (NBUF - 1)) * BUFB, idx_pro[1]);
+      issue_data(lds + ((b0 + 2) & (NBUF - 1)) * BUFB, idx_pro[2]);
+      idx_cur = idx_pro[3];
+      barrier_after<waitcnt_imm(LPW, 0)>();  // blocks b0, b0+1 (and the queries) have landed
       bf16x8_t kf[KS];
       kprefetch(lds + (b0 & (NBUF - 1)) * BUFB, kf);
       f32x16_t s0 = score_mfmas(lds + (b0 & (NBUF - 1)) * BUFB, kf, [](auto) {});
@@ -683,55 +690,87 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
       lds_st(sbuf + 16 * l32 + 4 * wave, m_run);
       lds_st(sbuf + 512 + 16 * l32 + 4 * wave, l_own);
     }
-    barrier_after<waitcnt_imm(VM_ANY, 0)>();
-    f32x4_t mrow = lds_ld<f32x4_t>(sbuf + 16 * l32);
-    f32x4_t lrow = lds_ld<f32x4_t>(sbuf + 512 + 16 * l32);
-    const int fo = 128 * wave + 4 * hl;
-    // lane's rows: tile row 32 rg + l32; its 16 bytes of a 512-feature row at
-    // 128 wave + 32 fb + 8 gq + 4 hl
-    auto row_live = [&](int rg) { return t * MT + rg * 32 + l32 < g.R; };
-    auto write_out = [&](const f32x4_t& lr, const f32x4_t& mr) {
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        if (!row_live(rg)) continue;
-        const size_t orow = (size_t)g.q0 * p.H + t * MT + rg * 32 + l32;
-        const float inv = 1.f / lr[rg];
-        __bf16* out = static_cast<__bf16*>(p.out) + orow * DV + fo;
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb) {
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            bf16x4_t v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[rg][fb][4 * gq + e] * inv);
-            *reinterpret_cast<bf16x4_t*>(out + 32 * fb + 8 * gq) = v4;
-          }
-        }
-        if (wave == 0 && hl == 0 && p.lse) p.lse[orow] = (mr[rg] + log2f(lr[rg])) * LN2;
-      }
-    };
+    // Every wave is done with the block buffers, and the gathers past the
+    // segment's end have landed: the buffers serve as staging space below.
+    barrier_after<waitcnt_imm(0, 0)>();
+    const f32x4_t mrow = lds_ld<f32x4_t>(sbuf + 16 * l32);
+    const f32x4_t lrow = lds_ld<f32x4_t>(sbuf + 512 + 16 * l32);
+    // The accumulator holds, in lane (l32, hl), features 32 fb + 8 gq + 4 hl
+    // .. +3 of this wave's 128 (fo = 128 wave) for tile row 32 rg + l32: a
+    // store straight from it would touch 32 rows per instruction.  The wave
+    // stages its slab [rows][128 features] in its own part of the block
+    // buffers (rows padded by 16 bytes, so that the 16 rows of a write phase
+    // fall on distinct banks) and writes whole row segments from there.
+    // Within one wave LDS accesses execute in order: no waits between the
+    // staging writes, the reads and the next pass's writes.
+    const int fo = 128 * wave;
+    auto row_live = [&](int trow) { return t * MT + trow < g.R; };
     if (slot < 0) {
-      if (b_begin < b_end) write_out(lrow, mrow);  // empty split segments leave the output alone
+      if (b_begin < b_end) {  // empty split segments leave the output alone
+        // bf16 rows of 256 bytes, all 128 rows in one pass
+        constexpr int STR = 256 + 16;
+        lds_char* stg = lds + wave * (MT * STR);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          const float inv = 1.f / lrow[rg];
+#pragma unroll
+          for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              bf16x4_t v4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[rg][fb][4 * gq + e] * inv);
+              lds_st(stg + (32 * rg + l32) * STR + 2 * (32 * fb + 8 * gq + 4 * hl), v4);
+            }
+        }
+        // 16 lanes per row, 4 rows per instruction
+        __bf16* out = static_cast<__bf16*>(p.out) + ((size_t)g.q0 * p.H + t * MT) * DV + fo + 8 * (lane & 15);
+#pragma unroll 8
+        for (int i = 0; i < MT / 4; ++i) {
+          const int trow = 4 * i + (lane >> 4);
+          const bf16x8_t v = lds_ld<bf16x8_t>(stg + trow * STR + 16 * (lane & 15));
+          if (row_live(trow)) *reinterpret_cast<bf16x8_t*>(out + (size_t)trow * DV) = v;
+        }
+        if (p.lse && wave == 0 && hl == 0) {
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg)
+            if (row_live(32 * rg + l32))
+              p.lse[(size_t)g.q0 * p.H + t * MT + 32 * rg + l32] = (mrow[rg] + log2f(lrow[rg])) * LN2;
+        }
+      }
       continue;
     }
     {
+      // fp32 partial rows (512 bytes of this wave's features), 64 rows per pass
+      constexpr int STR = 512 + 16;
+      lds_char* stg = lds + wave * (64 * STR);
       float* base = p.ws + slot * slot_floats(MT);
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        const int trow = rg * 32 + l32;
-        float* ob = base + (size_t)trow * DV + fo;
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int fb = 0; fb < FB; ++fb) {
+        for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            float4 v4 = make_float4(o[rg][fb][4 * gq], o[rg][fb][4 * gq + 1], o[rg][fb][4 * gq + 2],
-                                    o[rg][fb][4 * gq + 3]);
-            *reinterpret_cast<float4*>(ob + 32 * fb + 8 * gq) = v4;
-          }
+          for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x16_t& x = o[2 * h + r2][fb];
+              const f32x4_t v4 = {x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]};
+              lds_st(stg + (32 * r2 + l32) * STR + 4 * (32 * fb + 8 * gq + 4 * hl), v4);
+            }
+        // 32 lanes per row, 2 rows per instruction
+        float* ob = base + (size_t)(64 * h) * DV + fo + 4 * l32;
+#pragma unroll 8
+        for (int i = 0; i < 32; ++i) {
+          const int r = 2 * i + hl;
+          const f32x4_t v = lds_ld<f32x4_t>(stg + r * STR + 16 * l32);
+          *reinterpret_cast<f32x4_t*>(ob + (size_t)r * DV) = v;
         }
-        if (wave == 0 && hl == 0) {
-          base[(size_t)MT * DV + trow] = mrow[rg];
-          base[(size_t)MT * DV + MT + trow] = lrow[rg];
+      }
+      if (wave == 0 && hl == 0) {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          base[(size_t)MT * DV + 32 * rg + l32] = mrow[rg];
+          base[(size_t)MT * DV + MT + 32 * rg + l32] = lrow[rg];
         }
       }
     }
