@@ -71,6 +71,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef short __attribute__((ext_vector_type(4))) i16x4_t;
+typedef uint32_t __attribute__((ext_vector_type(4))) u32x4_t;
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int NWAVE = 4;           // waves per workgroup, 32 own rows each
@@ -459,31 +460,48 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
       mb = max3(max3(s[9], s[10], s[11]), max3(s[12], s[13], s[14]), max3(s[15], mb, mb));
       here(mb);
     };
-    auto sm_ref = [&]() {
+    // the new reference, in three dependent stages
+    float m_new = 0.f;
+    auto sm_ref1 = [&]() {
       mb = fmaxf(mb, other_half(mb)) * c;  // c > 0
+      here(mb);
+    };
+    auto sm_ref2 = [&]() {
       const bool move = mb > m_run + RESCALE_SLACK;  // also true while m_run is -inf
-      const float m_new = move ? mb : m_run;
+      m_new = move ? mb : m_run;
       // rows that keep their reference get exactly 1 (also when it is still -inf)
       alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      here(m_new);
+      here(alpha);
+    };
+    auto sm_ref3 = [&]() {
       l_run *= alpha;
       m_run = m_new;
       mu = m_run == -INFINITY ? 0.f : m_run;  // all columns masked so far
       here(mu);
-      here(alpha);
       here(l_run);
     };
-    // weights of columns x, x + 1 (x even) under the reference
-    auto sm_exp2 = [&](const f32x16_t& s, int x, bf16x8_t& pk0, bf16x8_t& pk1) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[x], c, -mu));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[x + 1], c, -mu));
-      const bf16x2_t two = {(__bf16)e0, (__bf16)e1};
-      l_run += e0;
-      l_run += e1;
-      bf16x8_t& pk = x < 8 ? pk0 : pk1;
-      pk[x & 7] = two[0];
-      pk[(x & 7) + 1] = two[1];
+    // weight of column x under the reference; the weights of columns x - 1
+    // and x (x odd) go out as one packed bf16 pair, pw[x >> 1]
+    uint32_t pw[8];
+    float e_even = 0.f;
+    auto sm_exp = [&](const f32x16_t& s, auto xc) {
+      constexpr int x = decltype(xc)::value;
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[x], c, -mu));
+      l_run += e;
       here(l_run);
-      here(pk);
+      if constexpr (x & 1) {
+        const bf16x2_t two = {(__bf16)e_even, (__bf16)e};
+        pw[x >> 1] = __builtin_bit_cast(uint32_t, two);
+        here(pw[x >> 1]);
+      } else {
+        e_even = e;
+        here(e_even);
+      }
+    };
+    auto sm_pack = [&](bf16x8_t& pk0, bf16x8_t& pk1) {
+      pk0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+      pk1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]});
     };
 
     auto score_mfmas = [&](const lds_char* kbuf, bf16x8_t* kf, auto&& under) {
@@ -538,10 +556,12 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
       sm_mask(s0, b0);
       sm_max0(s0);
       sm_max1(s0);
-      sm_ref();
+      sm_ref1();
+      sm_ref2();
+      sm_ref3();
       alpha = 1.f;  // O is still zero: no factor to apply
-#pragma unroll
-      for (int x = 0; x < 16; x += 2) sm_exp2(s0, x, pc0, pc1);
+      static_for<0, 16>([&](auto xc) { sm_exp(s0, xc); });
+      sm_pack(pc0, pc1);
     }
 
     // ------------------------------------------------------------------
@@ -634,7 +654,6 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
       }
 
       // ---- phase B: values of block b, softmax of block b+1 ----
-      bf16x8_t pn0 = bf16x8_t{}, pn1 = bf16x8_t{};
       const lds_char* nb0 = nbuf + kofs0;
       const lds_char* nb1 = nbuf + kofs1;
       // step i: k2 = i >> 4, fb = (i >> 2) & 3, rg = i & 3
@@ -648,19 +667,23 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
         }
         if constexpr (k2 == 0 && fb == 2) pf[1][rg] = pread(rg, 1);
         value_mfma(o[rg][fb], vf[k2][fb], pf[k2][rg]);
+        // the softmax of block b+1, spread so that no step carries more
+        // VALU work than one MFMA covers; the dependent stages of the new
+        // reference sit two steps apart
         if constexpr (i == 0 && MASK) sm_mask(sn, b + 1);
         if constexpr (i == 1) sm_max0(sn);
         if constexpr (i == 2) sm_max1(sn);
-        if constexpr (i == 3) sm_ref();
-        if constexpr (i >= 4 && i < 12) sm_exp2(sn, 2 * (i - 4), pn0, pn1);
+        if constexpr (i == 3) sm_ref1();
+        if constexpr (i == 5) sm_ref2();
+        if constexpr (i == 7) sm_ref3();
+        if constexpr (i >= 8 && i < 24) sm_exp(sn, std::integral_constant<int, i - 8>{});
         if constexpr (i >= 2 * FB * RG - KDEPTH) {
           constexpr int k = i - (2 * FB * RG - KDEPTH);
           kpre[k] = lds_ld<bf16x8_t>((k & 1 ? nb1 : nb0) + 2048 * (k >> 1));
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-      pc0 = pn0;
-      pc1 = pn1;
+      sm_pack(pc0, pc1);
       idx_cur = idx_next;
       // the accumulators leave the iteration settled: whatever the compiler
       // places between iterations (or after the loop) may touch them
