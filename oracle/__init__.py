@@ -14,11 +14,14 @@ Each function is a plain, slow, obviously-correct statement of one stage:
 * ``attention.verify_request``   fp64 masked softmax over the absorbed-MLA
                                  576-d latents, output = weighted c_kv;
 * ``accept.accept``              greedy root walk along the target argmax,
-                                 plus a brute-force path enumerator.
+                                 plus a brute-force path enumerator;
+* ``commit.batch``               committing the accepted path into the paged
+                                 cache (new slot lists; optional compaction
+                                 of the accepted latent rows).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 against brute force, closed forms, hand-derived fixtures or an independent
 library routine (see each test module's docstring).  No function is
 "parity unpinned".
 """
-from . import accept, attention, tree, visibility  # noqa: F401
+from . import accept, attention, commit, tree, visibility  # noqa: F401
