@@ -2,12 +2,13 @@
  * ddtree.h -- C ABI of libddtree.so: the DDTree tree-verify hot path on
  * AMD Instinct MI355X (gfx950).
  *
- * Four stages of one speculative verify step, in the order a caller runs them:
+ * The stages of one speculative verify step, in the order a caller runs them:
  *   ddtree_build_tree          best-first draft tree from per-depth top-k log-probs
  *   ddtree_compile_visibility  ancestor-or-self bitsets (+ positions, + dense mask)
  *   ddtree_verify_attn         absorbed-MLA attention of every tree node x head
  *                              over the shared prefix plus its own ancestors
  *   ddtree_accept              greedy walk along the target argmax
+ *   ddtree_commit_kv           the accepted path into the KV cache (after accept)
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -224,6 +225,52 @@ int ddtree_accept(const int32_t* node_tokens, const int32_t* node_parents,
                   const int32_t* qo_indptr, const int32_t* target_predict, int bs, int depth_max,
                   int32_t* accepted_nodes, int32_t* accept_len, int32_t* commit_tokens,
                   int32_t* bonus_tokens, void* stream);
+
+/*
+ * ddtree_commit_kv -- the accepted path enters each request's KV cache.
+ *
+ * Defined by "The Architecture of a Speculative Decoding Engine ...",
+ * sections "The First Attempt: Temporary Buffers and Post-Verify Compaction"
+ * (the tree nodes' latents are appended after the prefix for verification;
+ * afterwards the accepted ones are gathered from their scattered places into
+ * contiguous positions), "The Off-by-One Labyrinth" (the bonus token is not
+ * cached) and "The Final Resolution: A Concrete Trace" (the accepted nodes,
+ * root included, are committed: the cache grows by accept_len).
+ *
+ *   kv_indptr [bs+1], kv_indices: request r's slot list, its P_r prefix slots
+ *                then the slots of its Q_r tree nodes in node order (the
+ *                ddtree_verify_attn layout).
+ *   qo_indptr [bs+1]; accepted_nodes [bs, depth_max+1] and accept_len [bs]
+ *                as ddtree_accept writes them (path root first).
+ *   max_kv_len   >= every request's slot-list length (sizes the launch).
+ *   new_kv_indptr [bs+1] i32 out: new_kv_indptr[0] = 0, request r's new list
+ *                has P_r + accept_len_r entries.
+ *   new_kv_indices [new_kv_capacity] i32 out: request r's new list = its
+ *                prefix slots, then
+ *                  index form (kv_pool NULL): the slots of the path's nodes
+ *                    in path order -- no latent moves;
+ *                  move form (kv_pool given): its first accept_len node slots,
+ *                    after the latent row of the path's i-th node has been
+ *                    copied into the i-th node slot (rows read before they
+ *                    are overwritten: the compaction the page describes).
+ *                Either way the new list reads the prefix latents, then the
+ *                accepted nodes' latents in path order.  Entries past
+ *                new_kv_capacity are not written; the old total
+ *                kv_indptr[bs] - kv_indptr[0] always suffices.  Must not
+ *                overlap kv_indices.
+ *   kv_pool      nullable [num_slots, 576] rows of dtype (DDTREE_BF16 or
+ *                DDTREE_F32), modified in place by the move form.
+ * Errors: EINVAL (null required pointer, bs < 0, depth_max < 0,
+ * max_kv_len < 1, new_kv_capacity < 0, bad dtype or num_slots with a pool),
+ * EUNSUPPORTED (max_kv_len above 65535 * 8192).  Device data that disagrees
+ * is clamped (accept_len to [0, min(Q_r, depth_max+1)], node ids to the
+ * request, slots to the pool); the affected outputs are unspecified.
+ */
+int ddtree_commit_kv(const int32_t* kv_indptr, const int32_t* kv_indices,
+                     const int32_t* qo_indptr, const int32_t* accepted_nodes,
+                     const int32_t* accept_len, int bs, int depth_max, int max_kv_len,
+                     int32_t* new_kv_indptr, int32_t* new_kv_indices, long long new_kv_capacity,
+                     void* kv_pool, long long num_slots, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,9 +28,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(ddtree_[a-z_0-9]+)\s*\(", text)))
 
 
-def test_header_declares_the_four_stages():
+def test_header_declares_the_stages():
     names = declared_functions()
-    for n in ("ddtree_build_tree", "ddtree_compile_visibility", "ddtree_verify_attn", "ddtree_accept"):
+    for n in ("ddtree_build_tree", "ddtree_compile_visibility", "ddtree_verify_attn", "ddtree_accept",
+              "ddtree_commit_kv"):
         assert n in names
 
 
@@ -112,6 +113,27 @@ def test_accept_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 1, -1, FAKE, FAKE, FAKE, FAKE, NULL) == EINVAL
     assert f(FAKE, NULL, FAKE, FAKE, 1, 7, FAKE, FAKE, FAKE, FAKE, NULL) == EINVAL
     assert f(NULL, NULL, NULL, NULL, 0, 7, NULL, NULL, NULL, NULL, NULL) == 0
+
+
+def test_commit_kv_validation(lib):
+    f = lib.ddtree_commit_kv
+    args = dict(kvp=FAKE, kvi=FAKE, qo=FAKE, nodes=FAKE, alen=FAKE, bs=1, D=7, maxkv=100, nkvp=FAKE,
+                nkvi=FAKE, cap=100, pool=NULL, nslots=0, dtype=_lib.DDTREE_BF16, stream=NULL)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+    assert call(bs=-1) == EINVAL
+    assert call(kvi=NULL) == EINVAL
+    assert call(nkvp=NULL) == EINVAL
+    assert call(D=-1) == EINVAL
+    assert call(maxkv=0) == EINVAL
+    assert call(cap=-1) == EINVAL
+    assert call(pool=FAKE, nslots=0) == EINVAL          # a pool needs slots
+    assert call(pool=FAKE, nslots=10, dtype=7) == EINVAL
+    assert call(maxkv=2**31 - 1) == EUNSUPPORTED        # more than 65535 prefix chunks
+    assert "commit_kv" in _err(lib)
+    assert call(bs=0, kvp=NULL, kvi=NULL, qo=NULL, nodes=NULL, alen=NULL, nkvp=NULL, nkvi=NULL) == 0
 
 
 def test_binding_rejects_host_tensors():

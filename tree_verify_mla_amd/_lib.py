@@ -54,6 +54,9 @@ def load() -> ctypes.CDLL:
     lib.ddtree_verify_attn.argtypes = [P, P, I64, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P, SZ, P]
     lib.ddtree_accept.restype = I
     lib.ddtree_accept.argtypes = [P, P, P, P, I, I, P, P, P, P, P]
+    lib.ddtree_commit_kv.restype = I
+    lib.ddtree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, P, P, ctypes.c_longlong, P,
+                                     ctypes.c_longlong, I, P]
     _lib = lib
     return lib
 
@@ -146,3 +149,28 @@ def ddtree_accept(node_tokens, node_parents, qo_indptr, target_predict, depth_ma
         bs, int(depth_max), _p(accepted_nodes, torch.int32, "accepted_nodes"),
         _p(accept_len, torch.int32, "accept_len"), _p(commit_tokens, torch.int32, "commit_tokens"),
         _p(bonus_tokens, torch.int32, "bonus_tokens"), _stream(stream)))
+
+
+def ddtree_commit_kv(kv_indptr, kv_indices, qo_indptr, accepted_nodes, accept_len,
+                     max_kv_len: int, new_kv_indptr, new_kv_indices, kv_pool=None, stream=None):
+    """Index form without ``kv_pool``; move form (rows compacted in place) with it."""
+    bs = qo_indptr.numel() - 1
+    depth_max = accepted_nodes.shape[1] - 1
+    pool_ptr, nslots, dt = None, 0, DDTREE_BF16
+    if kv_pool is not None:
+        if kv_pool.dtype == torch.bfloat16:
+            dt = DDTREE_BF16
+        elif kv_pool.dtype == torch.float32:
+            dt = DDTREE_F32
+        else:
+            raise TypeError("kv_pool must be bfloat16 or float32")
+        if kv_pool.dim() != 2 or kv_pool.shape[1] != 576:
+            raise ValueError("kv_pool must be [num_slots, 576]")
+        pool_ptr, nslots = _p(kv_pool, kv_pool.dtype, "kv_pool"), int(kv_pool.shape[0])
+    _check("ddtree_commit_kv", load().ddtree_commit_kv(
+        _p(kv_indptr, torch.int32, "kv_indptr"), _p(kv_indices, torch.int32, "kv_indices"),
+        _p(qo_indptr, torch.int32, "qo_indptr"), _p(accepted_nodes, torch.int32, "accepted_nodes"),
+        _p(accept_len, torch.int32, "accept_len"), bs, int(depth_max), int(max_kv_len),
+        _p(new_kv_indptr, torch.int32, "new_kv_indptr"),
+        _p(new_kv_indices, torch.int32, "new_kv_indices"), int(new_kv_indices.numel()),
+        pool_ptr, nslots, dt, _stream(stream)))

@@ -1,4 +1,5 @@
-"""One DDTree verify step on device tensors: build -> visibility -> attention -> accept.
+"""One DDTree verify step on device tensors: build -> visibility -> attention -> accept
+(-> commit of the accepted paths into the KV slot lists).
 
 ``VerifyStep`` owns the output and workspace tensors (torch allocations, made
 once) and enqueues the four library calls on the current stream with no host
@@ -74,6 +75,9 @@ class VerifyStep:
         self.accept_len = torch.empty(x.bs, **i32)
         self.commit_tokens = torch.empty(x.bs, D + 1, **i32)
         self.bonus_tokens = torch.empty(x.bs, **i32)
+        # the committed slot lists (never longer than the verify lists)
+        self.new_kv_indptr = torch.empty(x.bs + 1, **i32)
+        self.new_kv_indices = torch.empty(max(x.kv_indices.numel(), 1), **i32)
 
     def build(self, stream=None):
         x = self.x
@@ -100,6 +104,14 @@ class VerifyStep:
         _lib.ddtree_accept(self.node_tokens, self.node_parents, x.qo_indptr, tp, x.depth,
                            self.accepted_nodes, self.accept_len, self.commit_tokens,
                            self.bonus_tokens, stream=stream)
+
+    def commit(self, kv_pool=None, stream=None):
+        """Commit the accepted paths into new slot lists: index form, or with
+        ``kv_pool`` the move form (accepted rows compacted in that pool, in place)."""
+        x = self.x
+        _lib.ddtree_commit_kv(x.kv_indptr, x.kv_indices, x.qo_indptr, self.accepted_nodes,
+                              self.accept_len, x.max_kv_len, self.new_kv_indptr,
+                              self.new_kv_indices, kv_pool=kv_pool, stream=stream)
 
     def run(self, stream=None):
         """All four stages (accept needs ``target_predict`` in the inputs)."""
