@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Params p) {
   }
 }
 
-// Merge of a tile's partial slots: one wavefront per output row (4 rows per
-// workgroup).  Lane l owns features 8l .. 8l+7 of the row.  The segments are
+// Merge of the fp32 kernel's split tiles (row-major partial slots): one
+// wavefront per output row (4 rows per workgroup).  Lane l owns features 8l .. 8l+7 of the row.  The segments are
 // taken MERGE_BATCH at a time: their m, l and partial-output loads are all
 // issued before any is used, then folded in segment order by an online
 // log-sum-exp (the order is fixed, so the result does not depend on timing).
@@ -115,6 +115,30 @@ __device__ inline long long merge_slot(const Params& p, long long k, long long f
   return 2 * w + (range_begin(w, U, Ge) >= tile_start ? 0 : 1);
 }
 
+// The split segments of tile t of request r: their count and what
+// merge_slot needs.  False when the tile needs no merge (one workgroup
+// covered it and wrote the output itself).
+struct MergePlan {
+  long long nseg, first_slot, w_first, tile_start, U, Ge;
+};
+__device__ inline bool merge_plan(const Params& p, int r, int t, const Geom& g, int mt, int G,
+                                  MergePlan& m) {
+  m.first_slot = 0, m.w_first = 0, m.tile_start = 0, m.U = 0, m.Ge = 1;
+  if (p.S > 0) {
+    m.nseg = p.S;
+    m.first_slot = ((long long)r * p.T_max + t) * p.S;
+    return true;
+  }
+  m.U = units_before(p.bs, p.qo, p.kvp, p.H, mt);
+  if (m.U <= 0) return false;
+  m.Ge = effective_groups(m.U, G);
+  m.tile_start = units_before(r, p.qo, p.kvp, p.H, mt) + (long long)t * g.NB;
+  m.w_first = group_of(m.tile_start, m.U, m.Ge);
+  const long long w_last = group_of(m.tile_start + g.NB - 1, m.U, m.Ge);
+  m.nseg = w_last - m.w_first + 1;
+  return w_last != m.w_first;
+}
+
 __global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt, int G, int dtype) {
   const int groups = (mt + MERGE_ROWS - 1) / MERGE_ROWS;
   const int tile = blockIdx.x / groups, rgrp = blockIdx.x % groups;
@@ -124,21 +148,9 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt
   if (t >= g.T) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = rgrp * MERGE_ROWS + wave;  // row inside the tile
-  long long first_slot = 0, w_first = 0, tile_start = 0, U = 0, Ge = 1;
-  long long nseg;
-  if (p.S > 0) {
-    nseg = p.S;
-    first_slot = ((long long)r * p.T_max + t) * p.S;
-  } else {
-    U = units_before(p.bs, p.qo, p.kvp, p.H, mt);
-    if (U <= 0) return;
-    Ge = effective_groups(U, G);
-    tile_start = units_before(r, p.qo, p.kvp, p.H, mt) + (long long)t * g.NB;
-    w_first = group_of(tile_start, U, Ge);
-    const long long w_last = group_of(tile_start + g.NB - 1, U, Ge);
-    if (w_first == w_last) return;  // one workgroup covered the tile and wrote it
-    nseg = w_last - w_first + 1;
-  }
+  MergePlan m;
+  if (!merge_plan(p, r, t, g, mt, G, m)) return;
+  const long long nseg = m.nseg;
   if (t * mt + row >= g.R) return;  // after the wave-cooperative sums above
   const long long sf = slot_floats(mt);
 
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt
 #pragma unroll
     for (int j = 0; j < MERGE_BATCH; ++j) {
       if (k0 + j < nseg) {
-        const float* base = p.ws + merge_slot(p, k0 + j, first_slot, w_first, tile_start, U, Ge) * sf;
+        const float* base = p.ws + merge_slot(p, k0 + j, m.first_slot, m.w_first, m.tile_start, m.U, m.Ge) * sf;
         ms[j] = base[(long long)mt * DV + row];
         ls[j] = base[(long long)mt * DV + mt + row];
         const float4* o = reinterpret_cast<const float4*>(base + (long long)row * DV + 8 * lane);
@@ -187,6 +199,95 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt
   if (lane == 0 && p.lse) p.lse[orow] = (M + log2f(L)) * LN2;
 }
 
+// Merge of the matrix-core kernel's split tiles.  That kernel stores a
+// partial in its accumulators' lane layout: wave w's store (rg, fb, gq)
+// writes 1 KB contiguously, lane l's 16 bytes holding features
+// 128 w + 32 fb + 8 gq + 4 (l >> 5) .. +3 of tile row 32 rg + (l & 31).
+// One wavefront per (tile, row group rg, feature quarter w) reads exactly
+// those runs (16 loads of 1 KB per segment), so lane l folds the segments for
+// its own row with the same ordered log-sum-exp as merge_kernel, the loads of
+// LANES_BATCH segments issued before any is used.  The bf16 output goes
+// through LDS and leaves as 256-byte row segments.
+constexpr int LANES_BATCH = 2;
+constexpr int LANES_STR = 256 + 16;  // bytes per staged row (padded: no bank conflicts)
+
+__global__ __launch_bounds__(64) void merge_lanes_kernel(Params p, int G) {
+  constexpr int mt = MT_BF16, RG = 4, FB = 4;
+  typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  __shared__ __align__(16) char stg[32 * LANES_STR];
+  const int q = blockIdx.x & 15, tile = blockIdx.x >> 4;
+  const int rg = q >> 2, w = q & 3;
+  const int r = tile / p.T_max, t = tile % p.T_max;
+  if (r >= p.bs) return;
+  const Geom g = geom(p.qo, p.kvp, r, p.H, mt);
+  if (t >= g.T) return;
+  MergePlan m;
+  if (!merge_plan(p, r, t, g, mt, G, m)) return;
+  const int lane = threadIdx.x, l32 = lane & 31, hl = lane >> 5;
+  const int row = 32 * rg + l32;  // tile row of this lane
+  const long long sf = slot_floats(mt);
+  const long long run = ((long long)(w * RG + rg) * FB * 4) * 256 + 4 * lane;
+
+  float M = -INFINITY, L = 0.f;
+  float acc[64];
+#pragma unroll
+  for (int e = 0; e < 64; ++e) acc[e] = 0.f;
+  for (long long k0 = 0; k0 < m.nseg; k0 += LANES_BATCH) {
+    float ms[LANES_BATCH], ls[LANES_BATCH];
+    float4 x[LANES_BATCH][16];
+#pragma unroll
+    for (int j = 0; j < LANES_BATCH; ++j) {
+      if (k0 + j < m.nseg) {
+        const float* base =
+            p.ws + merge_slot(p, k0 + j, m.first_slot, m.w_first, m.tile_start, m.U, m.Ge) * sf;
+        ms[j] = base[(long long)mt * DV + row];
+        ls[j] = base[(long long)mt * DV + mt + row];
+        const float4* src = reinterpret_cast<const float4*>(base + run);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[j][c] = src[c * 64];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < LANES_BATCH; ++j) {
+      if (k0 + j >= m.nseg || ms[j] == -INFINITY) continue;  // a segment that saw no column
+      const float Mn = fmaxf(M, ms[j]);
+      const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
+      const float b = exp2f(ms[j] - Mn);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        acc[4 * c] = acc[4 * c] * a + x[j][c].x * b;
+        acc[4 * c + 1] = acc[4 * c + 1] * a + x[j][c].y * b;
+        acc[4 * c + 2] = acc[4 * c + 2] * a + x[j][c].z * b;
+        acc[4 * c + 3] = acc[4 * c + 3] * a + x[j][c].w * b;
+      }
+      L = L * a + ls[j] * b;
+      M = Mn;
+    }
+  }
+  const float inv = 1.f / L;
+  // chunk c = 4 fb + gq holds features 32 fb + 8 gq + 4 hl .. +3 of the quarter
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * c + e] * inv);
+    *reinterpret_cast<bf16x4*>(stg + l32 * LANES_STR + 2 * (32 * (c >> 2) + 8 * (c & 3) + 4 * hl)) = v;
+  }
+  __syncthreads();
+  const size_t row0 = (size_t)g.q0 * p.H + (size_t)t * mt + 32 * rg;  // output row of tile row 32 rg
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // 16 lanes per row, 4 rows per instruction
+    const int tr = 4 * i + (lane >> 4);
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + tr * LANES_STR + 16 * (lane & 15));
+    if (t * mt + 32 * rg + tr < g.R)
+      *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + (row0 + tr) * DV + 128 * w +
+                                 8 * (lane & 15)) = v;
+  }
+  if (p.lse && w == 0 && hl == 0 && t * mt + row < g.R)
+    p.lse[row0 + l32] = (M + log2f(L)) * LN2;
+}
+
 }  // namespace
 
 int launch_f32(const Params& p, int grid, hipStream_t s) {
@@ -195,6 +296,11 @@ int launch_f32(const Params& p, int grid, hipStream_t s) {
 }
 
 int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s) {
+  if (mt == MT_BF16) {  // the matrix-core kernel's lane-layout partials (bf16 output)
+    const long long groups = (long long)p.bs * p.T_max * 16;
+    hipLaunchKernelGGL(merge_lanes_kernel, dim3((unsigned)groups), dim3(64), 0, s, p, grid_groups);
+    return check_launch("verify_attn(merge)");
+  }
   const long long groups = (long long)p.bs * p.T_max * ((mt + MERGE_ROWS - 1) / MERGE_ROWS);
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)groups), dim3(64 * MERGE_ROWS), 0, s, p, mt,
                      grid_groups, dtype);
@@ -255,7 +361,8 @@ extern "C" int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t nu
   const int mt = dtype == DDTREE_BF16 ? MT_BF16 : MT_F32;
   const long long T_max = ((long long)max_q_len * num_heads + mt - 1) / mt;
   DDTREE_REQUIRE(T_max * bs * (num_splits > 0 ? num_splits : 1) < (1LL << 31) &&
-                     T_max * bs * ((mt + MERGE_ROWS - 1) / MERGE_ROWS) < (1LL << 31),
+                     T_max * bs * ((mt + MERGE_ROWS - 1) / MERGE_ROWS) < (1LL << 31) &&
+                     T_max * bs * 16 < (1LL << 31),
                  DDTREE_EUNSUPPORTED, "verify_attn: grid too large");
 
   Params p;

@@ -764,31 +764,22 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
       continue;
     }
     {
-      // fp32 partial rows (512 bytes of this wave's features), 64 rows per pass
-      constexpr int STR = 512 + 16;
-      lds_char* stg = lds + wave * (64 * STR);
+      // fp32 partial in the accumulator's lane layout: store (rg, fb, gq) of
+      // wave w writes 1 KB contiguously, lane l's 16 bytes (features
+      // 128 w + 32 fb + 8 gq + 4 (l >> 5) .. +3 of tile row 32 rg + (l & 31))
+      // at float offset (((w RG + rg) FB + fb) 4 + gq) 256 + 4 l.
       float* base = p.ws + slot * slot_floats(MT);
+      float* ob = base + (size_t)wave * (RG * FB * 4 * 256) + 4 * lane;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
+        for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-          for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const f32x16_t& x = o[2 * h + r2][fb];
-              const f32x4_t v4 = {x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]};
-              lds_st(stg + (32 * r2 + l32) * STR + 4 * (32 * fb + 8 * gq + 4 * hl), v4);
-            }
-        // 32 lanes per row, 2 rows per instruction
-        float* ob = base + (size_t)(64 * h) * DV + fo + 4 * l32;
-#pragma unroll 8
-        for (int i = 0; i < 32; ++i) {
-          const int r = 2 * i + hl;
-          const f32x4_t v = lds_ld<f32x4_t>(stg + r * STR + 16 * l32);
-          *reinterpret_cast<f32x4_t*>(ob + (size_t)r * DV) = v;
-        }
-      }
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x16_t& x = o[rg][fb];
+            const f32x4_t v4 = {x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]};
+            *reinterpret_cast<f32x4_t*>(ob + ((rg * FB + fb) * 4 + gq) * 256) = v4;
+          }
       if (wave == 0 && hl == 0) {
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
