@@ -5,13 +5,19 @@
 // columns into blocks of KB.  One work unit = (row tile, KV block).
 //
 // Two schedules:
-//  * persistent (num_splits == 0): the grid's G workgroups take equal
-//    contiguous ranges of the global unit list (requests in order, tiles in
-//    order, blocks fastest).  A workgroup's range is a sequence of segments,
-//    each inside one tile; a segment that covers its whole tile writes the
-//    final output, any other writes a partial (unnormalised O, running max,
+//  * persistent (num_splits == 0): the grid's G workgroups take contiguous
+//    ranges of the global unit list (requests in order, tiles in order,
+//    blocks fastest).  A workgroup's range is a sequence of segments, each
+//    inside one tile; a segment that covers its whole tile writes the final
+//    output, any other writes a partial (unnormalised O, running max,
 //    running sum) into workspace slot 2*w + (first segment of w ? 0 : 1).
-//    Small problems use fewer workgroups (at least MIN_UNITS units each).
+//    The ranges are equal in cost, not in units: every tile is preceded by
+//    KAPPA virtual units that stand for the cost of starting a segment
+//    (loading the rows' queries, filling the block pipeline, storing the
+//    output), and the virtual unit list is split evenly.  A range that
+//    crosses a tile boundary, and so runs one segment more, gets about KAPPA
+//    real units fewer.  Small problems use fewer workgroups (at least
+//    MIN_UNITS units each).
 //  * split (num_splits == S >= 1): workgroup (r, t, s) takes blocks
 //    [s*NB/S, (s+1)*NB/S) of tile t; S == 1 writes final output, S > 1
 //    writes slot (r * T_max + t) * S + s.
@@ -31,6 +37,7 @@ constexpr int LATENT = 576;
 constexpr int DV = 512;
 constexpr int KB = 32;          // KV columns per work unit
 constexpr int MIN_UNITS = 8;    // smallest persistent range per workgroup
+constexpr int KAPPA = 8;        // virtual units ahead of every tile (cost of a segment start)
 constexpr int MT_BF16 = 128;    // rows per tile, bf16 matrix-core kernel (4 waves x 32 rows)
 constexpr int MT_F32 = 4;       // rows per tile, fp32 kernel
 
@@ -78,6 +85,11 @@ __device__ inline Geom geom(const int32_t* qo, const int32_t* kvp, int r, int H,
 }
 
 __device__ inline long long units_of(const Geom& g) { return (long long)g.T * g.NB; }
+// real units, or virtual units (each tile KAPPA longer)
+template <bool VIRT>
+__device__ inline long long units_w(const Geom& g) {
+  return (long long)g.T * (g.NB + (VIRT ? KAPPA : 0));
+}
 
 __device__ inline long long shfl_ll(long long v, int src) {
   int lo = __shfl((int)(v & 0xffffffffLL), src);
@@ -91,14 +103,16 @@ __device__ inline long long shfl_up_ll(long long v, int d) {
   return ((long long)hi << 32) | (unsigned int)lo;
 }
 
-// Wave-cooperative (all 64 lanes call it): units of requests [0, rmax).
+// Wave-cooperative (all 64 lanes call it): real (or virtual) units of
+// requests [0, rmax).
+template <bool VIRT = false>
 __device__ inline long long units_before(int rmax, const int32_t* qo, const int32_t* kvp, int H,
                                          int mt) {
   const int lane = threadIdx.x & 63;
   long long tot = 0;
   for (int r0 = 0; r0 < rmax; r0 += 64) {
     const int r = r0 + lane;
-    long long u = r < rmax ? units_of(geom(qo, kvp, r, H, mt)) : 0;
+    long long u = r < rmax ? units_w<VIRT>(geom(qo, kvp, r, H, mt)) : 0;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       int lo = __shfl_xor((int)(u & 0xffffffffLL), off);
@@ -110,15 +124,16 @@ __device__ inline long long units_before(int rmax, const int32_t* qo, const int3
   return tot;
 }
 
-// Wave-cooperative: request r whose unit range [start, start + units) holds
-// unit u (r = bs if u is past the end).
+// Wave-cooperative: request r whose real (or virtual) unit range
+// [start, start + units) holds unit u (r = bs if u is past the end).
+template <bool VIRT = false>
 __device__ inline void locate(long long u, const int32_t* qo, const int32_t* kvp, int bs, int H,
                               int mt, int& r_out, long long& start_out) {
   const int lane = threadIdx.x & 63;
   long long base = 0;
   for (int r0 = 0; r0 < bs; r0 += 64) {
     const int r = r0 + lane;
-    const long long ur = r < bs ? units_of(geom(qo, kvp, r, H, mt)) : 0;
+    const long long ur = r < bs ? units_w<VIRT>(geom(qo, kvp, r, H, mt)) : 0;
     long long incl = ur;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -145,12 +160,30 @@ __device__ inline int effective_groups(long long U, int G) {
   return (int)(g < G ? g : G);
 }
 
-// first unit of workgroup w under the persistent schedule
-__device__ inline long long range_begin(long long w, long long U, long long Ge) { return w * U / Ge; }
+// first (virtual) unit of workgroup w under the persistent schedule, V the
+// virtual total
+__device__ inline long long range_begin(long long w, long long V, long long Ge) { return w * V / Ge; }
 
-// workgroup whose persistent range holds unit u
-__device__ inline long long group_of(long long u, long long U, long long Ge) {
-  return ((u + 1) * Ge + U - 1) / U - 1;
+// Wave-cooperative: the real unit at virtual position x (the first real unit
+// at or after it: a position inside a tile's KAPPA prefix maps to the tile's
+// first unit; x >= the virtual total maps to the real total U).
+__device__ inline long long real_of(long long x, long long U, const int32_t* qo, const int32_t* kvp,
+                                   int bs, int H, int mt) {
+  int r;
+  long long vstart;
+  locate<true>(x, qo, kvp, bs, H, mt, r, vstart);
+  r = __builtin_amdgcn_readfirstlane(r);
+  if (r >= bs) return U;
+  const Geom g = geom(qo, kvp, r, H, mt);
+  const long long local = x - vstart;
+  const long long t = local / (g.NB + KAPPA), off = local % (g.NB + KAPPA);
+  const long long ustart = units_before(r, qo, kvp, H, mt);
+  return ustart + t * g.NB + (off > KAPPA ? off - KAPPA : 0);
+}
+
+// workgroup whose persistent range holds virtual position x (V the total)
+__device__ inline long long group_of(long long x, long long V, long long Ge) {
+  return ((x + 1) * Ge + V - 1) / V - 1;
 }
 
 }  // namespace attn

@@ -106,35 +106,39 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Params p) {
 constexpr int MERGE_ROWS = 4;   // rows per merge workgroup (= waves)
 constexpr int MERGE_BATCH = 4;  // segments whose loads are in flight together
 
-// workspace slot of segment k of tile t of request r
+// workspace slot of segment k of tile t of request r (persistent schedule:
+// workgroup w_first + k; its first segment lies in this tile exactly when its
+// virtual range starts at or after the tile's virtual start vtile)
 __device__ inline long long merge_slot(const Params& p, long long k, long long first_slot,
-                                       long long w_first, long long tile_start, long long U,
+                                       long long w_first, long long vtile, long long V,
                                        long long Ge) {
   if (p.S > 0) return first_slot + k;
   const long long w = w_first + k;
-  return 2 * w + (range_begin(w, U, Ge) >= tile_start ? 0 : 1);
+  return 2 * w + (range_begin(w, V, Ge) >= vtile ? 0 : 1);
 }
 
 // The split segments of tile t of request r: their count and what
 // merge_slot needs.  False when the tile needs no merge (one workgroup
 // covered it and wrote the output itself).
 struct MergePlan {
-  long long nseg, first_slot, w_first, tile_start, U, Ge;
+  long long nseg, first_slot, w_first, vtile, V, Ge;
 };
 __device__ inline bool merge_plan(const Params& p, int r, int t, const Geom& g, int mt, int G,
                                   MergePlan& m) {
-  m.first_slot = 0, m.w_first = 0, m.tile_start = 0, m.U = 0, m.Ge = 1;
+  m.first_slot = 0, m.w_first = 0, m.vtile = 0, m.V = 1, m.Ge = 1;
   if (p.S > 0) {
     m.nseg = p.S;
     m.first_slot = ((long long)r * p.T_max + t) * p.S;
     return true;
   }
-  m.U = units_before(p.bs, p.qo, p.kvp, p.H, mt);
-  if (m.U <= 0) return false;
-  m.Ge = effective_groups(m.U, G);
-  m.tile_start = units_before(r, p.qo, p.kvp, p.H, mt) + (long long)t * g.NB;
-  m.w_first = group_of(m.tile_start, m.U, m.Ge);
-  const long long w_last = group_of(m.tile_start + g.NB - 1, m.U, m.Ge);
+  const long long U = units_before(p.bs, p.qo, p.kvp, p.H, mt);
+  if (U <= 0) return false;
+  m.Ge = effective_groups(U, G);
+  m.V = units_before<true>(p.bs, p.qo, p.kvp, p.H, mt);
+  // the tile's virtual start; its real units follow the KAPPA prefix
+  m.vtile = units_before<true>(r, p.qo, p.kvp, p.H, mt) + (long long)t * (g.NB + KAPPA);
+  m.w_first = group_of(m.vtile + KAPPA, m.V, m.Ge);
+  const long long w_last = group_of(m.vtile + KAPPA + g.NB - 1, m.V, m.Ge);
   m.nseg = w_last - m.w_first + 1;
   return w_last != m.w_first;
 }
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt
 #pragma unroll
     for (int j = 0; j < MERGE_BATCH; ++j) {
       if (k0 + j < nseg) {
-        const float* base = p.ws + merge_slot(p, k0 + j, m.first_slot, m.w_first, m.tile_start, m.U, m.Ge) * sf;
+        const float* base = p.ws + merge_slot(p, k0 + j, m.first_slot, m.w_first, m.vtile, m.V, m.Ge) * sf;
         ms[j] = base[(long long)mt * DV + row];
         ls[j] = base[(long long)mt * DV + mt + row];
         const float4* o = reinterpret_cast<const float4*>(base + (long long)row * DV + 8 * lane);
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p, int G) {
     for (int j = 0; j < LANES_BATCH; ++j) {
       if (k0 + j < m.nseg) {
         const float* base =
-            p.ws + merge_slot(p, k0 + j, m.first_slot, m.w_first, m.tile_start, m.U, m.Ge) * sf;
+            p.ws + merge_slot(p, k0 + j, m.first_slot, m.w_first, m.vtile, m.V, m.Ge) * sf;
         ms[j] = base[(long long)mt * DV + row];
         ls[j] = base[(long long)mt * DV + mt + row];
         const float4* src = reinterpret_cast<const float4*>(base + run);

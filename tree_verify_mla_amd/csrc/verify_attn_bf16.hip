@@ -266,8 +266,11 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
     Ge = effective_groups(U, gridDim.x);
     if (blockIdx.x >= Ge) return;
     if (Ge == gridDim.x && (Ge & 7) == 0) v = (blockIdx.x & 7) * (Ge >> 3) + (blockIdx.x >> 3);
-    u0 = range_begin(v, U, Ge);
-    u1 = range_begin(v + 1, U, Ge);
+    // equal shares of the virtual unit list (segment starts cost KAPPA units)
+    const long long V = uni64(units_before<true>(p.bs, p.qo, p.kvp, p.H, MT));
+    u0 = uni64(real_of(range_begin(v, V, Ge), U, p.qo, p.kvp, p.bs, p.H, MT));
+    u1 = uni64(real_of(range_begin(v + 1, V, Ge), U, p.qo, p.kvp, p.bs, p.H, MT));
+    if (u0 >= u1) return;  // a share that holds no real unit
   }
 
   // A range is a run of segments, each inside one tile.  Only the first can
