@@ -97,6 +97,12 @@ __device__ inline long long shfl_ll(long long v, int src) {
   return ((long long)hi << 32) | (unsigned int)lo;
 }
 
+__device__ inline long long shfl_xor_ll(long long v, int m) {
+  int lo = __shfl_xor((int)(v & 0xffffffffLL), m);
+  int hi = __shfl_xor((int)(v >> 32), m);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
 __device__ inline long long shfl_up_ll(long long v, int d) {
   int lo = __shfl_up((int)(v & 0xffffffffLL), d);
   int hi = __shfl_up((int)(v >> 32), d);

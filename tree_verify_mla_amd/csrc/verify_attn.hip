@@ -203,19 +203,57 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt
   if (lane == 0 && p.lse) p.lse[orow] = (M + log2f(L)) * LN2;
 }
 
+// merge_plan for the persistent schedule in one pass over the requests (one
+// global round trip instead of one per sum): the real and virtual unit
+// totals, and the virtual units before request r.  Wave-cooperative.
+__device__ inline bool merge_plan_fast(const Params& p, int r, int t, const Geom& g, int mt, int G,
+                                       MergePlan& m) {
+  if (p.S > 0) return merge_plan(p, r, t, g, mt, G, m);
+  const int lane = threadIdx.x & 63;
+  long long U = 0, V = 0, vb = 0;
+  for (int r0 = 0; r0 < p.bs; r0 += 64) {
+    const int rr = r0 + lane;
+    long long u = 0, vu = 0;
+    if (rr < p.bs) {
+      const Geom gg = geom(p.qo, p.kvp, rr, p.H, mt);
+      u = units_w<false>(gg);
+      vu = units_w<true>(gg);
+    }
+    long long before = rr < r ? vu : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      u += shfl_xor_ll(u, off);
+      vu += shfl_xor_ll(vu, off);
+      before += shfl_xor_ll(before, off);
+    }
+    U += u;
+    V += vu;
+    vb += before;
+  }
+  if (U <= 0) return false;
+  m.first_slot = 0;
+  m.Ge = effective_groups(U, G);
+  m.V = V;
+  m.vtile = vb + (long long)t * (g.NB + KAPPA);
+  m.w_first = group_of(m.vtile + KAPPA, m.V, m.Ge);
+  const long long w_last = group_of(m.vtile + KAPPA + g.NB - 1, m.V, m.Ge);
+  m.nseg = w_last - m.w_first + 1;
+  return w_last != m.w_first;
+}
+
 // Merge of the matrix-core kernel's split tiles.  That kernel stores a
 // partial in its accumulators' lane layout: wave w's store (rg, fb, gq)
 // writes 1 KB contiguously, lane l's 16 bytes holding features
 // 128 w + 32 fb + 8 gq + 4 (l >> 5) .. +3 of tile row 32 rg + (l & 31).
-// One wavefront per (tile, row group rg, feature quarter w) reads exactly
-// those runs (16 loads of 1 KB per segment), so lane l folds the segments for
-// its own row with the same ordered log-sum-exp as merge_kernel, the loads of
-// LANES_BATCH segments issued before any is used.  The bf16 output goes
-// through LDS and leaves as 256-byte row segments.
-constexpr int LANES_BATCH = 2;
+// One workgroup per (tile, row group rg, feature quarter w); its wave h reads
+// the runs of fb = 2h, 2h + 1 (8 loads of 1 KB per segment), so lane l folds
+// the segments for its own row with the same ordered log-sum-exp as
+// merge_kernel, the loads of LANES_BATCH segments issued before any is used.
+// The bf16 output goes through LDS and leaves as 256-byte row segments.
+constexpr int LANES_BATCH = 4;
 constexpr int LANES_STR = 256 + 16;  // bytes per staged row (padded: no bank conflicts)
 
-__global__ __launch_bounds__(64) void merge_lanes_kernel(Params p, int G) {
+__global__ __launch_bounds__(128) void merge_lanes_kernel(Params p, int G) {
   constexpr int mt = MT_BF16, RG = 4, FB = 4;
   typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -227,19 +265,20 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p, int G) {
   const Geom g = geom(p.qo, p.kvp, r, p.H, mt);
   if (t >= g.T) return;
   MergePlan m;
-  if (!merge_plan(p, r, t, g, mt, G, m)) return;
-  const int lane = threadIdx.x, l32 = lane & 31, hl = lane >> 5;
+  if (!merge_plan_fast(p, r, t, g, mt, G, m)) return;
+  const int lane = threadIdx.x & 63, h = threadIdx.x >> 6, l32 = lane & 31, hl = lane >> 5;
   const int row = 32 * rg + l32;  // tile row of this lane
   const long long sf = slot_floats(mt);
-  const long long run = ((long long)(w * RG + rg) * FB * 4) * 256 + 4 * lane;
+  // chunk c = 4 fb + gq of the wave's runs: c in [8 h, 8 h + 8)
+  const long long run = ((long long)(w * RG + rg) * FB * 4 + 8 * h) * 256 + 4 * lane;
 
   float M = -INFINITY, L = 0.f;
-  float acc[64];
+  float acc[32];
 #pragma unroll
-  for (int e = 0; e < 64; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 32; ++e) acc[e] = 0.f;
   for (long long k0 = 0; k0 < m.nseg; k0 += LANES_BATCH) {
     float ms[LANES_BATCH], ls[LANES_BATCH];
-    float4 x[LANES_BATCH][16];
+    float4 x[LANES_BATCH][8];
 #pragma unroll
     for (int j = 0; j < LANES_BATCH; ++j) {
       if (k0 + j < m.nseg) {
@@ -249,7 +288,7 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p, int G) {
         ls[j] = base[(long long)mt * DV + mt + row];
         const float4* src = reinterpret_cast<const float4*>(base + run);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) x[j][c] = src[c * 64];
+        for (int c = 0; c < 8; ++c) x[j][c] = src[c * 64];
       }
     }
 #pragma unroll
@@ -259,7 +298,7 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p, int G) {
       const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
       const float b = exp2f(ms[j] - Mn);
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
+      for (int c = 0; c < 8; ++c) {
         acc[4 * c] = acc[4 * c] * a + x[j][c].x * b;
         acc[4 * c + 1] = acc[4 * c + 1] * a + x[j][c].y * b;
         acc[4 * c + 2] = acc[4 * c + 2] * a + x[j][c].z * b;
@@ -270,25 +309,26 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p, int G) {
     }
   }
   const float inv = 1.f / L;
-  // chunk c = 4 fb + gq holds features 32 fb + 8 gq + 4 hl .. +3 of the quarter
+  // chunk c = 8 h + c' holds features 32 fb + 8 gq + 4 hl .. +3 of the quarter
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
+  for (int cc = 0; cc < 8; ++cc) {
+    const int c = 8 * h + cc;
     bf16x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * c + e] * inv);
+    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * cc + e] * inv);
     *reinterpret_cast<bf16x4*>(stg + l32 * LANES_STR + 2 * (32 * (c >> 2) + 8 * (c & 3) + 4 * hl)) = v;
   }
   __syncthreads();
   const size_t row0 = (size_t)g.q0 * p.H + (size_t)t * mt + 32 * rg;  // output row of tile row 32 rg
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {  // 16 lanes per row, 4 rows per instruction
-    const int tr = 4 * i + (lane >> 4);
+  for (int i = 0; i < 4; ++i) {  // 16 lanes per row, 4 rows per instruction, 16 rows per wave
+    const int tr = 16 * h + 4 * i + (lane >> 4);
     const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + tr * LANES_STR + 16 * (lane & 15));
     if (t * mt + 32 * rg + tr < g.R)
       *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + (row0 + tr) * DV + 128 * w +
                                  8 * (lane & 15)) = v;
   }
-  if (p.lse && w == 0 && hl == 0 && t * mt + row < g.R)
+  if (p.lse && w == 0 && h == 0 && hl == 0 && t * mt + row < g.R)
     p.lse[row0 + l32] = (M + log2f(L)) * LN2;
 }
 
@@ -302,7 +342,7 @@ int launch_f32(const Params& p, int grid, hipStream_t s) {
 int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s) {
   if (mt == MT_BF16) {  // the matrix-core kernel's lane-layout partials (bf16 output)
     const long long groups = (long long)p.bs * p.T_max * 16;
-    hipLaunchKernelGGL(merge_lanes_kernel, dim3((unsigned)groups), dim3(64), 0, s, p, grid_groups);
+    hipLaunchKernelGGL(merge_lanes_kernel, dim3((unsigned)groups), dim3(128), 0, s, p, grid_groups);
     return check_launch("verify_attn(merge)");
   }
   const long long groups = (long long)p.bs * p.T_max * ((mt + MERGE_ROWS - 1) / MERGE_ROWS);
