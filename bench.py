@@ -98,8 +98,8 @@ def measured_traffic(workload: str):
     copy_kib = float(kv["copy_bytes"]) / 1024.0
     f_fac = copy_kib / float(kv["copy.FETCH_SIZE"])
     w_fac = copy_kib / float(kv["copy.WRITE_SIZE"])
-    fetch = sum(float(kv[f"{k}.FETCH_SIZE"]) for k in ("attn_bf16_kernel", "merge_kernel"))
-    write = sum(float(kv[f"{k}.WRITE_SIZE"]) for k in ("attn_bf16_kernel", "merge_kernel"))
+    fetch = sum(float(kv[f"{k}.FETCH_SIZE"]) for k in ("attn_bf16_kernel", "merge_lanes_kernel"))
+    write = sum(float(kv[f"{k}.WRITE_SIZE"]) for k in ("attn_bf16_kernel", "merge_lanes_kernel"))
     return {"fetch_bytes": fetch * 1024.0 * f_fac, "write_bytes": write * 1024.0 * w_fac,
             "fetch_factor": f_fac, "write_factor": w_fac}
 
@@ -121,6 +121,40 @@ def algorithmic_work(wl, depths):
         nbytes += Q * H * (576 + 512) * elt + Q * H * 4      # q in, out + lse
         nbytes += Q * W * 4                                   # ancestor bitsets
     return flops, nbytes
+
+
+def commit_bytes(wl, accept_len, move: bool) -> int:
+    """Bytes ddtree_commit_kv needs: the prefix slot ids read and written, the
+    path entries, node slots and new entries, the per-request scalars, and in
+    the move form each moved latent row read and written once."""
+    row = 576 * (2 if wl.dtype == "bf16" else 4)
+    n = 0
+    for r in range(wl.bs):
+        P, a = int(wl.prefix_lens[r]), int(accept_len[r])
+        n += 8 * P + 12 * a + 5 * 4
+        if move:
+            n += 2 * row * max(a - 1, 0)
+    return n + 4 * (wl.bs + 1)
+
+
+def time_commit(steps, K, stream, move: bool):
+    """Average duration (ms) of ddtree_commit_kv over K calls (HIP events on
+    the launch stream), rotating the instances like the main loop."""
+    import torch
+
+    R = len(steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(3):
+        st = steps[i % R]
+        st.commit(kv_pool=st.x.kv_pool if move else None, stream=stream)
+    torch.cuda.synchronize()
+    for i in range(K):
+        st = steps[i % R]
+        ev[i][0].record(stream)
+        st.commit(kv_pool=st.x.kv_pool if move else None, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(e[0].elapsed_time(e[1]) for e in ev) / K
 
 
 def cpu_baseline(wls, budget_s: float):
@@ -243,6 +277,14 @@ def main():
     attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     acc_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
 
+    # the KV commit after acceptance (not part of a step): index form, then
+    # the move form, last, since it compacts the instances' pools in place
+    alens = [st.accept_len.cpu().numpy() for st in steps]
+    cb_i = sum(commit_bytes(wls[k], alens[k], False) for k in range(R)) / R
+    cb_m = sum(commit_bytes(wls[k], alens[k], True) for k in range(R)) / R
+    commit_i_ms = time_commit(steps, K, stream, move=False)
+    commit_m_ms = time_commit(steps, K, stream, move=True)
+
     achieved = flops / (attn_ms * 1e-3) / 1e12
     traffic = measured_traffic(wls[0].name)
     value = flops / (step_ms * 1e-3) / 1e12
@@ -265,7 +307,7 @@ def main():
                    "q_len": int(wls[0].max_q_len), "prefix": int(wls[0].prefix_lens.max()),
                    "topk": wls[0].topk, "pool_slots": wls[0].num_slots, "instances": R,
                    "num_splits": args.num_splits, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "ddtree_verify_attn (attn_bf16_kernel + merge_kernel)",
+        "roofline": {"bound": "mfma", "kernel": "ddtree_verify_attn (attn_bf16_kernel + merge_lanes_kernel)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if traffic is None else round(traffic["fetch_bytes"] + traffic["write_bytes"]),
@@ -274,7 +316,15 @@ def main():
         "extra": {"attn_ms": round(attn_ms, 5), "build_visibility_ms": round(tv_ms, 5),
                   "accept_ms": round(acc_ms, 5),
                   "attn_GBps": round(gbps, 1), "attn_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
-                  "tree_steps_per_s": round(wls[0].bs / (step_ms * 1e-3), 1)},
+                  "tree_steps_per_s": round(wls[0].bs / (step_ms * 1e-3), 1),
+                  "commit_kv": {
+                      "index_form_us": round(commit_i_ms * 1e3, 2),
+                      "index_form_bytes": round(cb_i),
+                      "index_form_GBps": round(cb_i / (commit_i_ms * 1e-3) / 1e9, 1),
+                      "move_form_us": round(commit_m_ms * 1e3, 2),
+                      "move_form_bytes": round(cb_m),
+                      "move_form_GBps": round(cb_m / (commit_m_ms * 1e-3) / 1e9, 1),
+                      "hbm_peak_GBps": PEAK_HBM_GBPS}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wls, args.cpu_seconds)
