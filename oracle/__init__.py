@@ -17,11 +17,13 @@ Each function is a plain, slow, obviously-correct statement of one stage:
                                  plus a brute-force path enumerator;
 * ``commit.batch``               committing the accepted path into the paged
                                  cache (new slot lists; optional compaction
-                                 of the accepted latent rows).
+                                 of the accepted latent rows);
+* ``drafter.batch``              per-depth top-k log-probabilities of the
+                                 drafter's logits (fp64 log-softmax).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 against brute force, closed forms, hand-derived fixtures or an independent
 library routine (see each test module's docstring).  No function is
 "parity unpinned".
 """
-from . import accept, attention, commit, tree, visibility  # noqa: F401
+from . import accept, attention, commit, drafter, tree, visibility  # noqa: F401
