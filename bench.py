@@ -302,7 +302,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wls[0].dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; random latents, drafter top-k from N(0,1) logits)",
+        "data": "synthetic (seeded; random latents, drawn drafter top-k tables)",
         "config": {"workload": wls[0].name, "bs": wls[0].bs, "heads": wls[0].heads,
                    "q_len": int(wls[0].max_q_len), "prefix": int(wls[0].prefix_lens.max()),
                    "topk": wls[0].topk, "pool_slots": wls[0].num_slots, "instances": R,

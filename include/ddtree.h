@@ -3,6 +3,7 @@
  * AMD Instinct MI355X (gfx950).
  *
  * The stages of one speculative verify step, in the order a caller runs them:
+ *   ddtree_drafter_topk        per-depth top-k log-probs of the drafter's logits
  *   ddtree_build_tree          best-first draft tree from per-depth top-k log-probs
  *   ddtree_compile_visibility  ancestor-or-self bitsets (+ positions, + dense mask)
  *   ddtree_verify_attn         absorbed-MLA attention of every tree node x head
@@ -266,6 +267,33 @@ int ddtree_accept(const int32_t* node_tokens, const int32_t* node_parents,
  * is clamped (accept_len to [0, min(Q_r, depth_max+1)], node ids to the
  * request, slots to the pool); the affected outputs are unspecified.
  */
+/*
+ * ddtree_drafter_topk -- per-depth top-k log-probabilities of the drafter's
+ * logits (the input of ddtree_build_tree).
+ *
+ * Defined by "The DDTree CUDA Graph Fix ...", section "The DDTree
+ * Architecture: Confirming Multiple-Path Evaluation" (from each depth
+ * position's hidden state the vocabulary head yields the top-k candidate
+ * tokens with their log-probabilities).  Reading: the log-probability is the
+ * log-softmax over the whole vocabulary; the top k are the k largest in
+ * descending order, equal values in ascending token id.
+ *
+ *   logits   [rows, vocab] of dtype (DDTREE_F32 or DDTREE_BF16), row-major;
+ *            rows = bs * depth_max for a batch of drafts.  Finite or -inf.
+ *   topk_logprobs [rows, topk] f32 out; topk_ids [rows, topk] i32 out
+ *            (exactly the layout ddtree_build_tree reads).
+ *   workspace of ddtree_drafter_topk_workspace_size(rows, vocab, topk)
+ *            bytes (per-chunk statistics and candidates), caller-owned.
+ * Computed in fp32 (hardware exp and log); the order is decided on the
+ * logits themselves.  Errors: EINVAL (null pointer, rows < 0, bad dtype,
+ * topk outside [1, vocab]), EUNSUPPORTED (topk > 32, or more than 1024 chunk
+ * candidates: ceil(vocab / 8192) * topk > 1024), EWORKSPACE.
+ */
+size_t ddtree_drafter_topk_workspace_size(int rows, int vocab, int topk);
+int ddtree_drafter_topk(const void* logits, int dtype, int rows, int vocab, int topk,
+                        float* topk_logprobs, int32_t* topk_ids, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 int ddtree_commit_kv(const int32_t* kv_indptr, const int32_t* kv_indices,
                      const int32_t* qo_indptr, const int32_t* accepted_nodes,
                      const int32_t* accept_len, int bs, int depth_max, int max_kv_len,

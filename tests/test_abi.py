@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_stages():
     names = declared_functions()
     for n in ("ddtree_build_tree", "ddtree_compile_visibility", "ddtree_verify_attn", "ddtree_accept",
-              "ddtree_commit_kv"):
+              "ddtree_commit_kv", "ddtree_drafter_topk"):
         assert n in names
 
 
@@ -134,6 +134,25 @@ def test_commit_kv_validation(lib):
     assert call(maxkv=2**31 - 1) == EUNSUPPORTED        # more than 65535 prefix chunks
     assert "commit_kv" in _err(lib)
     assert call(bs=0, kvp=NULL, kvi=NULL, qo=NULL, nodes=NULL, alen=NULL, nkvp=NULL, nkvi=NULL) == 0
+
+
+def test_drafter_topk_validation(lib):
+    f = lib.ddtree_drafter_topk
+    F32 = _lib.DDTREE_F32
+    assert f(FAKE, F32, -1, 100, 8, FAKE, FAKE, FAKE, 1 << 20, NULL) == EINVAL
+    assert f(NULL, F32, 4, 100, 8, FAKE, FAKE, FAKE, 1 << 20, NULL) == EINVAL
+    assert f(FAKE, 9, 4, 100, 8, FAKE, FAKE, FAKE, 1 << 20, NULL) == EINVAL
+    assert f(FAKE, F32, 4, 100, 0, FAKE, FAKE, FAKE, 1 << 20, NULL) == EINVAL
+    assert f(FAKE, F32, 4, 5, 8, FAKE, FAKE, FAKE, 1 << 20, NULL) == EINVAL      # topk > vocab
+    assert f(FAKE, F32, 4, 100, 33, FAKE, FAKE, FAKE, 1 << 20, NULL) == EUNSUPPORTED
+    assert f(FAKE, F32, 4, 8192 * 200, 8, FAKE, FAKE, FAKE, 1 << 30, NULL) == EUNSUPPORTED
+    need = lib.ddtree_drafter_topk_workspace_size(4, 100, 8)
+    assert need == 4 * 1 * (2 + 16) * 4
+    assert lib.ddtree_drafter_topk_workspace_size(2, 8193, 3) == 2 * 2 * (2 + 6) * 4
+    assert f(FAKE, F32, 4, 100, 8, FAKE, FAKE, FAKE, need - 1, NULL) == EWORKSPACE
+    assert f(FAKE, F32, 4, 100, 8, FAKE, FAKE, NULL, need, NULL) == EWORKSPACE
+    assert "drafter_topk" in _err(lib)
+    assert f(NULL, F32, 0, 100, 8, NULL, NULL, NULL, 0, NULL) == 0
 
 
 def test_binding_rejects_host_tensors():

@@ -54,6 +54,10 @@ def load() -> ctypes.CDLL:
     lib.ddtree_verify_attn.argtypes = [P, P, I64, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P, SZ, P]
     lib.ddtree_accept.restype = I
     lib.ddtree_accept.argtypes = [P, P, P, P, I, I, P, P, P, P, P]
+    lib.ddtree_drafter_topk_workspace_size.restype = SZ
+    lib.ddtree_drafter_topk_workspace_size.argtypes = [I, I, I]
+    lib.ddtree_drafter_topk.restype = I
+    lib.ddtree_drafter_topk.argtypes = [P, I, I, I, I, P, P, P, SZ, P]
     lib.ddtree_commit_kv.restype = I
     lib.ddtree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, P, P, ctypes.c_longlong, P,
                                      ctypes.c_longlong, I, P]
@@ -174,3 +178,24 @@ def ddtree_commit_kv(kv_indptr, kv_indices, qo_indptr, accepted_nodes, accept_le
         _p(new_kv_indptr, torch.int32, "new_kv_indptr"),
         _p(new_kv_indices, torch.int32, "new_kv_indices"), int(new_kv_indices.numel()),
         pool_ptr, nslots, dt, _stream(stream)))
+
+
+def ddtree_drafter_topk_workspace_size(rows: int, vocab: int, topk: int) -> int:
+    return int(load().ddtree_drafter_topk_workspace_size(rows, vocab, topk))
+
+
+def ddtree_drafter_topk(logits, topk_logprobs, topk_ids, workspace=None, stream=None):
+    """logits [rows, vocab] (f32 or bf16) -> topk_logprobs [rows, k] f32, topk_ids [rows, k] i32."""
+    if logits.dtype == torch.bfloat16:
+        dt = DDTREE_BF16
+    elif logits.dtype == torch.float32:
+        dt = DDTREE_F32
+    else:
+        raise TypeError("logits must be bfloat16 or float32")
+    rows, vocab = logits.shape
+    k = topk_ids.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("ddtree_drafter_topk", load().ddtree_drafter_topk(
+        _p(logits, logits.dtype, "logits"), dt, rows, vocab, k,
+        _p(topk_logprobs, torch.float32, "topk_logprobs"), _p(topk_ids, torch.int32, "topk_ids"),
+        _p(workspace, None, "workspace"), ws_bytes, _stream(stream)))

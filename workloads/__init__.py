@@ -1,8 +1,8 @@
 """Seeded synthetic workloads for the DDTree tree-verify path.
 
 This package draws random inputs and lays them out in the shapes the verify
-step consumes.  It holds none of the method's own arithmetic (no tree search,
-no masking, no attention, no acceptance): both the CPU oracle and the HIP path
+step consumes.  It holds none of the method's own arithmetic (no log-softmax or
+top-k selection, no tree search, no masking, no attention, no acceptance): both the CPU oracle and the HIP path
 are fed from here, and neither imports the other.
 """
 from .configs import CONFIGS, Config, get_config  # noqa: F401
@@ -13,5 +13,6 @@ from .gen import (  # noqa: F401
     make_workload,
     draw_target_predict,
     draw_drafter_topk,
+    draw_drafter_logits,
     sensitize_tree_columns,
 )

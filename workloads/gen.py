@@ -4,10 +4,10 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order):
 
 1. ragged configs only: per-request prefix lengths ``P_r ~ U{lo..hi}``, then
    per-request budgets ``B_r`` uniform over the allowed choices;
-2. per request r, in request order: drafter logits ``N(0,1)[depth, vocab]``,
-   turned into log-probabilities (fp64 log-softmax), the top-``k`` entries per
-   depth in descending order with ties broken by ascending token id, stored
-   as fp32 values and int32 ids; then the root token ``U[0, vocab)``;
+2. per request r, in request order: the drafter's per-depth top-``k`` table
+   drawn directly (``draw_drafter_topk``: a first log-probability
+   ``-(3 + Exp(1))``, then ``Exp(0.3)`` gaps, rounded to fp32; distinct token
+   ids uniform over the vocabulary); then the root token ``U[0, vocab)``;
 3. one permutation of the slot pool: the first ``sum(P_r + Q_r)`` slots are
    dealt out request by request, ``P_r`` prefix slots then ``Q_r`` node slots
    (so ``kv_indices`` is the combined prefix ++ tree-node slot list);
@@ -19,8 +19,10 @@ bf16 workloads round q and the latent rows to bf16 with round-to-nearest-even
 and keep them as raw uint16 bit patterns.  Pool rows no request uses are NaN
 by default, so a stray read shows up in the output.
 
-The drafter top-k step is input synthesis here, not one of the verify path's
-stages; the module contains no tree search, mask, attention or acceptance.
+The top-k tables are drawn, not computed: log-softmax and top-k selection
+over logits are a stage of the method (``ddtree_drafter_topk``), whose
+inputs are raw logits (``draw_drafter_logits``).  The module contains no
+log-softmax, selection, tree search, mask, attention or acceptance.
 """
 from __future__ import annotations
 
@@ -115,14 +117,24 @@ class Workload:
 
 
 def draw_drafter_topk(rng: np.random.Generator, depth: int, topk: int, vocab: int):
-    """Per-depth top-k (descending, ties by id) of N(0,1) logits after fp64 log-softmax."""
-    logits = rng.standard_normal((depth, vocab))
-    mx = logits.max(axis=1, keepdims=True)
-    lse = mx + np.log(np.exp(logits - mx).sum(axis=1, keepdims=True))
-    logp = logits - lse
-    order = np.argsort(-logp, axis=1, kind="stable")[:, :topk]
-    vals = np.take_along_axis(logp, order, axis=1).astype(np.float32)
-    return vals, order.astype(np.int32)
+    """Per-depth top-k tables shaped like a drafter's, drawn directly: the
+    first log-probability is -(3 + Exp(1)), each next one lower by an Exp(0.3)
+    gap (non-increasing after rounding to fp32), and the token ids are
+    distinct, uniform over the vocabulary.  No softmax and no selection: those
+    are a stage of the method (ddtree_drafter_topk), whose inputs are the raw
+    logits of draw_drafter_logits."""
+    first = -(3.0 + rng.exponential(1.0, size=(depth, 1)))
+    gaps = rng.exponential(0.3, size=(depth, topk - 1))
+    vals = np.concatenate([first, first - np.cumsum(gaps, axis=1)], axis=1).astype(np.float32)
+    ids = np.stack([rng.choice(vocab, size=topk, replace=False) for _ in range(depth)])
+    return vals, ids.astype(np.int32)
+
+
+def draw_drafter_logits(rng: np.random.Generator, rows: int, vocab: int, std: float = 2.0,
+                        dtype: str = "f32") -> np.ndarray:
+    """Raw drafter logits N(0, std) [rows, vocab]: fp32, or bf16 bits (RNE)."""
+    x = (rng.standard_normal((rows, vocab)) * std).astype(np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
 def make_workload(cfg: Config, *, seed: Optional[int] = None, unused: str = "nan",
