@@ -157,6 +157,38 @@ def time_commit(steps, K, stream, move: bool):
     return sum(e[0].elapsed_time(e[1]) for e in ev) / K
 
 
+DRAFTER_VOCAB = 163840  # the pages give no vocabulary size: a large-model vocabulary
+
+
+def time_drafter_topk(wl, R: int, K: int, stream):
+    """Average duration (ms) of ddtree_drafter_topk on bs * depth rows of
+    DRAFTER_VOCAB fp32 logits (R rotated instances), and its bytes."""
+    import torch
+
+    from tree_verify_mla_amd import _lib
+    from workloads import draw_drafter_logits
+
+    rows, k = wl.bs * wl.depth, wl.topk
+    xs = [torch.from_numpy(draw_drafter_logits(np.random.default_rng(wl.seed + 7919 * (i + 1)), rows,
+                                               DRAFTER_VOCAB)).cuda() for i in range(R)]
+    vals = torch.empty(rows, k, dtype=torch.float32, device="cuda")
+    ids = torch.empty(rows, k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(_lib.ddtree_drafter_topk_workspace_size(rows, DRAFTER_VOCAB, k),
+                     dtype=torch.uint8, device="cuda")
+    for i in range(3):
+        _lib.ddtree_drafter_topk(xs[i % R], vals, ids, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        _lib.ddtree_drafter_topk(xs[i % R], vals, ids, workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    nbytes = rows * DRAFTER_VOCAB * 4 + rows * k * 8
+    return ms, rows, k, nbytes
+
+
 def cpu_baseline(wls, budget_s: float):
     """The CPU oracle as it stands, on whole requests of the workload (cycling
     through the rotated instances) until about budget_s seconds are used."""
@@ -284,6 +316,8 @@ def main():
     cb_m = sum(commit_bytes(wls[k], alens[k], True) for k in range(R)) / R
     commit_i_ms = time_commit(steps, K, stream, move=False)
     commit_m_ms = time_commit(steps, K, stream, move=True)
+    # the drafter's per-depth top-k (the stage before the tree build; not part of a step)
+    dk_ms, dk_rows, dk_k, dk_bytes = time_drafter_topk(wls[0], R, K, stream)
 
     achieved = flops / (attn_ms * 1e-3) / 1e12
     traffic = measured_traffic(wls[0].name)
@@ -324,7 +358,12 @@ def main():
                       "move_form_us": round(commit_m_ms * 1e3, 2),
                       "move_form_bytes": round(cb_m),
                       "move_form_GBps": round(cb_m / (commit_m_ms * 1e-3) / 1e9, 1),
-                      "hbm_peak_GBps": PEAK_HBM_GBPS}},
+                      "hbm_peak_GBps": PEAK_HBM_GBPS},
+                  "drafter_topk": {
+                      "rows": dk_rows, "vocab": DRAFTER_VOCAB, "k": dk_k, "dtype": "f32",
+                      "us": round(dk_ms * 1e3, 2), "bytes": dk_bytes,
+                      "GBps": round(dk_bytes / (dk_ms * 1e-3) / 1e9, 1),
+                      "hbm_frac": round(dk_bytes / (dk_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wls, args.cpu_seconds)

@@ -13,7 +13,8 @@
 // * chunk_kernel: workgroup (row, chunk) reads CHUNK consecutive logits of
 //   its row once (32 per thread, kept in registers) and writes the chunk's
 //   max m_c, its sum s_c of e^(x - m_c), and its k best (value, id) by k
-//   rounds of a workgroup argmax over the entries still in play;
+//   rounds of a workgroup argmax over the entries still in play (32-bit
+//   order keys, the smallest id among equal keys);
 // * merge_kernel: one wavefront per row folds the chunks in chunk order,
 //   M = max m_c, S = sum_c s_c e^(m_c - M), lse = M + log S, and takes the
 //   row's k best out of the chunks' candidates (the j-th best of a row is
@@ -35,22 +36,6 @@ constexpr int MERGE_PER_LANE = 16; // chunk candidates per lane in the merge (C 
 __device__ inline uint32_t fkey(float f) {
   const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);  // -0 ties with +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-// candidate key: larger value first, then smaller id; 0 = nothing
-__device__ inline unsigned long long ckey(float v, int id) {
-  return ((unsigned long long)fkey(v) << 32) | (uint32_t)(~(uint32_t)id);
-}
-__device__ inline int ckey_id(unsigned long long k) { return (int)~(uint32_t)(k & 0xffffffffu); }
-
-__device__ inline unsigned long long wave_max_u64(unsigned long long k) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)(k & 0xffffffffu), off);
-    const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off);
-    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-    k = o > k ? o : k;
-  }
-  return k;
 }
 __device__ inline float wave_max_f(float v) {
 #pragma unroll
@@ -76,6 +61,34 @@ __device__ inline int elem_of(int t, int j) {
   }
 }
 
+// the same with a runtime register index (arithmetic only)
+template <typename T, bool VEC>
+__device__ inline int elem_of_rt(int t, int j) {
+  if constexpr (VEC) {
+    constexpr int W = 16 / (int)sizeof(T);
+    return W * t + W * CT * (j / W) + j % W;
+  } else {
+    return t + CT * j;
+  }
+}
+
+// wave-wide maximum (MAX) or minimum of x, uniform result: DPP inside each
+// 16-lane row (swap neighbours, pairs, then mirror halves and rows), then
+// the four row results through scalar registers
+template <bool MAX>
+__device__ inline uint32_t wave_ext(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
 template <typename T>
 __device__ inline float to_f32(T x) {
   if constexpr (sizeof(T) == 2) return (float)x;
@@ -88,7 +101,8 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
                                                    float* __restrict__ ws_val,
                                                    int32_t* __restrict__ ws_id) {
   __shared__ float red_f[CT / 64];
-  __shared__ unsigned long long red_k[CT / 64];
+  __shared__ uint2 cand[CT / 64][KMAX];   // each wave's k best: (key, id)
+  __shared__ float cand_v[CT / 64][KMAX]; // and their logits
   const int row = blockIdx.x / C, c = blockIdx.x % C;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const long long c0 = (long long)c * CHUNK;          // first element of the chunk in its row
@@ -147,41 +161,88 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
     ws_ms[2 * slot + 1] = s;
   }
 
-  // k rounds of a workgroup argmax (larger value, then smaller id); an
-  // entry out of play has key 0
-  unsigned long long kk[EPT];
+  // The chunk's k best (the largest value, then the smallest id), in two
+  // steps without a barrier per round.  Keys are 32-bit order keys; 0 means
+  // nothing (every float's key is larger).
+  // 1. each wave takes its own k best.  A lane keeps its two best entries
+  //    (its registers hold ids in ascending order, so of equal keys the
+  //    first is the smaller id); a round is the wave maximum of the lanes'
+  //    first keys, then the smallest id among the lanes that hold it, and the
+  //    owner moves its second entry up.  A lane that has given up both looks
+  //    again, for the best entries after the last one it gave up in (key
+  //    descending, id ascending) order -- rare, and only that lane's wave
+  //    waits for it.
+  // 2. after one barrier, wave 0 takes the chunk's k best out of the 4 k
+  //    wave candidates in LDS the same way.
+  uint32_t key[EPT];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j)
-    kk[j] = ((live >> j) & 1u) ? ckey(x[j], (int)(c0 + elem_of<T, VEC>(t, j))) : 0ull;
-  // (registers are only ever indexed by unrolled constants: a runtime index
-  // would put the arrays in scratch memory)
-  for (int r = 0; r < k; ++r) {
-    unsigned long long best = 0;
-    float bx = 0.f;
+  for (int j = 0; j < EPT; ++j) key[j] = ((live >> j) & 1u) ? fkey(x[j]) : 0u;
+  // the two best entries after (bk, bj) in the order; bk = ~0u: from the top
+  auto best_two = [&](uint32_t lk, int lj, uint32_t& k1, int& j1, float& x1, uint32_t& k2,
+                      int& j2, float& x2) {
+    k1 = 0u, j1 = 0, x1 = 0.f, k2 = 0u, j2 = 0, x2 = 0.f;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-      const bool b = kk[j] > best;
-      best = b ? kk[j] : best;
-      bx = b ? x[j] : bx;
+      const uint32_t kj = (key[j] < lk || (key[j] == lk && j > lj)) ? key[j] : 0u;
+      const bool first = kj > k1, second = !first && kj > k2;
+      k2 = first ? k1 : (second ? kj : k2);
+      j2 = first ? j1 : (second ? j : j2);
+      x2 = first ? x1 : (second ? x[j] : x2);
+      k1 = first ? kj : k1;
+      j1 = first ? j : j1;
+      x1 = first ? x[j] : x1;
     }
-    const unsigned long long wbest = wave_max_u64(best);
-    __syncthreads();  // the previous round's readers are done with red_k
-    if (lane == 0) red_k[wave] = wbest;
-    __syncthreads();
-    unsigned long long g = red_k[0];
-#pragma unroll
-    for (int w = 1; w < CT / 64; ++w) g = red_k[w] > g ? red_k[w] : g;
-    // keys are unique (ids are), so exactly one thread owns a nonzero winner
-    if (g != 0) {
-      if (g == best) {
-        ws_val[slot * k + r] = bx;
-        ws_id[slot * k + r] = ckey_id(g);
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) kk[j] = kk[j] == g ? 0ull : kk[j];
+  };
+  uint32_t k1, k2;
+  int j1, j2;
+  float x1, x2;
+  best_two(0xffffffffu, -1, k1, j1, x1, k2, j2, x2);
+  for (int r = 0; r < k; ++r) {
+    const uint32_t myid = k1 ? (uint32_t)(c0 + elem_of_rt<T, VEC>(t, j1)) : 0xffffffffu;
+    const uint32_t wk = wave_ext<true>(k1);
+    const uint32_t wid = wave_ext<false>(k1 == wk ? myid : 0xffffffffu);
+    if (wk == 0u) {  // fewer than k logits in the wave
+      if (lane == 0) cand[wave][r] = make_uint2(0u, 0xffffffffu);
+    } else if (k1 == wk && myid == wid) {  // the owner
+      cand[wave][r] = make_uint2(wk, wid);
+      cand_v[wave][r] = x1;
+      if (k2 != 0u) {
+        k1 = k2, j1 = j2, x1 = x2, k2 = 0u;
+      } else {
+        best_two(k1, j1, k1, j1, x1, k2, j2, x2);
       }
-    } else if (t == 0) {  // fewer than k logits in the chunk
-      ws_val[slot * k + r] = -INFINITY;
-      ws_id[slot * k + r] = INT_MAX;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // wave 0: candidate i = (wave i / k, round i % k), two per lane
+  uint32_t ck[2], cid[2];
+  float cv[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = lane + 64 * q;
+    ck[q] = 0u, cid[q] = 0xffffffffu, cv[q] = 0.f;
+    if (i < (CT / 64) * k) {
+      const uint2 v = cand[i / k][i % k];
+      ck[q] = v.x, cid[q] = v.y, cv[q] = cand_v[i / k][i % k];
+    }
+  }
+  for (int r = 0; r < k; ++r) {
+    // the lane's best of its two (the larger key, then the smaller id)
+    const bool second = ck[1] > ck[0] || (ck[1] == ck[0] && cid[1] < cid[0]);
+    const uint32_t lk = second ? ck[1] : ck[0], lid = second ? cid[1] : cid[0];
+    const float lv = second ? cv[1] : cv[0];
+    const uint32_t gk = wave_ext<true>(lk);
+    const uint32_t gid = wave_ext<false>(lk == gk ? lid : 0xffffffffu);
+    if (gk == 0u) {
+      if (lane == 0) {
+        ws_val[slot * k + r] = -INFINITY;
+        ws_id[slot * k + r] = INT_MAX;
+      }
+    } else if (lk == gk && lid == gid) {
+      ws_val[slot * k + r] = lv;
+      ws_id[slot * k + r] = (int32_t)gid;
+      if (second) ck[1] = 0u; else ck[0] = 0u;
     }
   }
 }
@@ -192,6 +253,29 @@ __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __
                                                    float* __restrict__ out_val,
                                                    int32_t* __restrict__ out_id) {
   const int row = blockIdx.x, lane = threadIdx.x;
+  // the chunks' candidates, MERGE_PER_LANE per lane (candidate i in lane
+  // i % 64); k rounds as in the chunks: each lane keeps its two best (the
+  // larger key, then the smaller id), a round takes the wave maximum key and
+  // then the smallest id holding it, and the owner moves its second up (or,
+  // having given up both, looks again after the last one)
+  const int nc = C * k;
+  const float* cv = ws_val + (size_t)row * nc;
+  const int32_t* ci = ws_id + (size_t)row * nc;
+  uint32_t key[MERGE_PER_LANE], id[MERGE_PER_LANE];
+  float val[MERGE_PER_LANE];
+#pragma unroll
+  for (int q = 0; q < MERGE_PER_LANE; ++q) {
+    const int i = lane + 64 * q;
+    const bool in = i < nc;
+    const int32_t cid = in ? ci[i] : INT_MAX;  // both loads issued together:
+    const float cvv = in ? cv[i] : 0.f;        // neither waits for the other
+    const bool real = cid != INT_MAX;
+    val[q] = cvv;
+    key[q] = real ? fkey(cvv) : 0u;
+    id[q] = real ? (uint32_t)cid : 0xffffffffu;
+  }
+  // (the candidates' loads above are issued first: the two sets are
+  // independent, so the wave waits for memory once)
   const float* ms = ws_ms + (size_t)row * C * 2;
   // M = max m_c, then S = sum_c s_c e^(m_c - M) in chunk order (64 chunks at
   // a time, each batch summed by the same fixed shuffle tree)
@@ -205,37 +289,39 @@ __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __
   }
   const float lse = M + __logf(S);
 
-  // the chunks' candidates, MERGE_PER_LANE per lane (candidate i in lane i % 64)
-  const int nc = C * k;
-  const float* cv = ws_val + (size_t)row * nc;
-  const int32_t* ci = ws_id + (size_t)row * nc;
-  unsigned long long key[MERGE_PER_LANE];
-  float val[MERGE_PER_LANE];
-#pragma unroll
-  for (int q = 0; q < MERGE_PER_LANE; ++q) {
-    const int i = lane + 64 * q;
-    key[q] = 0;
-    val[q] = 0.f;
-    if (i < nc && ci[i] != INT_MAX) {
-      val[q] = cv[i];
-      key[q] = ckey(val[q], ci[i]);
-    }
-  }
-  for (int r = 0; r < k; ++r) {
-    unsigned long long best = 0;
-    float bv = 0.f;
+  // a lane's two best candidates after (lk, lid) in (key descending, id
+  // ascending) order; lk = ~0u: from the top (ids are unique)
+  auto best_two = [&](uint32_t lk, uint32_t lid, uint32_t& k1, uint32_t& i1, float& v1,
+                      uint32_t& k2, uint32_t& i2, float& v2) {
+    k1 = 0u, i1 = 0xffffffffu, v1 = 0.f, k2 = 0u, i2 = 0xffffffffu, v2 = 0.f;
 #pragma unroll
     for (int q = 0; q < MERGE_PER_LANE; ++q) {
-      const bool b = key[q] > best;
-      best = b ? key[q] : best;
-      bv = b ? val[q] : bv;
+      const bool after = key[q] < lk || (key[q] == lk && id[q] > lid);
+      const uint32_t kq = after ? key[q] : 0u;
+      const bool first = kq != 0u && (kq > k1 || (kq == k1 && id[q] < i1));
+      const bool second = !first && kq != 0u && (kq > k2 || (kq == k2 && id[q] < i2));
+      k2 = first ? k1 : (second ? kq : k2);
+      i2 = first ? i1 : (second ? id[q] : i2);
+      v2 = first ? v1 : (second ? val[q] : v2);
+      k1 = first ? kq : k1;
+      i1 = first ? id[q] : i1;
+      v1 = first ? val[q] : v1;
     }
-    const unsigned long long g = wave_max_u64(best);
-    if (g != 0 && g == best) {
-      out_val[(size_t)row * k + r] = bv - lse;
-      out_id[(size_t)row * k + r] = ckey_id(g);
-#pragma unroll
-      for (int q = 0; q < MERGE_PER_LANE; ++q) key[q] = key[q] == g ? 0ull : key[q];
+  };
+  uint32_t k1, i1, k2, i2;
+  float v1, v2;
+  best_two(0xffffffffu, 0u, k1, i1, v1, k2, i2, v2);
+  for (int r = 0; r < k; ++r) {
+    const uint32_t gk = wave_ext<true>(k1);
+    const uint32_t gid = wave_ext<false>(k1 == gk ? i1 : 0xffffffffu);
+    if (gk != 0u && k1 == gk && i1 == gid) {
+      out_val[(size_t)row * k + r] = v1 - lse;
+      out_id[(size_t)row * k + r] = (int32_t)gid;
+      if (k2 != 0u) {
+        k1 = k2, i1 = i2, v1 = v2, k2 = 0u;
+      } else {
+        best_two(k1, i1, k1, i1, v1, k2, i2, v2);
+      }
     }
   }
 }
