@@ -19,11 +19,14 @@ Each function is a plain, slow, obviously-correct statement of one stage:
                                  cache (new slot lists; optional compaction
                                  of the accepted latent rows);
 * ``drafter.batch``              per-depth top-k log-probabilities of the
-                                 drafter's logits (fp64 log-softmax).
+                                 drafter's logits (fp64 log-softmax);
+* ``sample.batch``               stochastic acceptance along the tree
+                                 (rejection sampling against the target
+                                 distribution, fixed-order fp32 sums).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 against brute force, closed forms, hand-derived fixtures or an independent
 library routine (see each test module's docstring).  No function is
 "parity unpinned".
 """
-from . import accept, attention, commit, drafter, tree, visibility  # noqa: F401
+from . import accept, attention, commit, drafter, sample, tree, visibility  # noqa: F401
