@@ -41,15 +41,19 @@ def _blocks(vocab: int):
     return [(b * per, min(vocab, (b + 1) * per)) for b in range(NT)]
 
 
+def _seq(values) -> np.ndarray:
+    """Running sums of fp32 values, added one by one from 0 (numpy's cumsum
+    accumulates in order, in the array's dtype)."""
+    return np.cumsum(np.asarray(values, dtype=np.float32), dtype=np.float32)
+
+
+def _block_masses(row: np.ndarray) -> list:
+    return [(_seq(row[lo:hi])[-1] if hi > lo else np.float32(0.0)) for lo, hi in _blocks(len(row))]
+
+
 def _mass(row: np.ndarray) -> np.float32:
     """Row mass in the fixed order (fp32)."""
-    total = np.float32(0.0)
-    for lo, hi in _blocks(len(row)):
-        bs = np.float32(0.0)
-        for j in range(lo, hi):
-            bs = np.float32(bs + row[j])
-        total = np.float32(total + bs)
-    return total
+    return _seq(_block_masses(row))[-1]
 
 
 def _inverse_cdf(row: np.ndarray, threshold: np.float32) -> int:
@@ -60,12 +64,7 @@ def _inverse_cdf(row: np.ndarray, threshold: np.float32) -> int:
     rounding leaves the threshold unreached inside that block, its last token
     with mass; if no block reaches it, the row's last token with mass."""
     blocks = _blocks(len(row))
-    masses = []
-    for lo, hi in blocks:
-        bs = np.float32(0.0)
-        for j in range(lo, hi):
-            bs = np.float32(bs + row[j])
-        masses.append(bs)
+    masses = _block_masses(row)
     run = np.float32(0.0)
     for (lo, hi), bs in zip(blocks, masses):
         if np.float32(run + bs) > threshold:
