@@ -9,6 +9,7 @@
  *   ddtree_verify_attn         absorbed-MLA attention of every tree node x head
  *                              over the shared prefix plus its own ancestors
  *   ddtree_accept              greedy walk along the target argmax
+ *   ddtree_tree_sample         (or) stochastic acceptance against the target distribution
  *   ddtree_commit_kv           the accepted path into the KV cache (after accept)
  *
  * Conventions shared by every entry point
@@ -226,6 +227,44 @@ int ddtree_accept(const int32_t* node_tokens, const int32_t* node_parents,
                   const int32_t* qo_indptr, const int32_t* target_predict, int bs, int depth_max,
                   int32_t* accepted_nodes, int32_t* accept_len, int32_t* commit_tokens,
                   int32_t* bonus_tokens, void* stream);
+
+/*
+ * ddtree_tree_sample -- stochastic (temperature) acceptance along the tree,
+ * the sampling counterpart of ddtree_accept.
+ *
+ * Defined by "The DDTree CUDA Graph Fix ...", section "Temperature Support:
+ * Already Working for Linear, Planned for DDTree" (tree-structured
+ * rejection sampling against the target's filtered distribution at every
+ * node, the draft being the tree's tokens).  Rule (speculative sampling for
+ * a draft with all its mass on its token): at node cur the residual starts
+ * as the target row, mass R; children are tried in node order; child c with
+ * token t is accepted iff coins[c] * R < res[t], otherwise R -= res[t] and
+ * res[t] = 0; the walk stops when no child is accepted or after
+ * depth_max + 1 nodes; the bonus is drawn from the residual at the last
+ * node by inverse CDF at bonus_uniforms[r] * R.  fp32 with every sum in one
+ * fixed order: rows cut into 256 contiguous blocks of ceil(vocab / 256)
+ * tokens, each block summed token by token and the blocks one by one; the
+ * inverse CDF picks the first block whose running mass plus its own exceeds
+ * the threshold, then the first token of it whose running mass does (its
+ * last token with mass if rounding leaves it unreached; the row's last
+ * token with mass if no block reaches it).
+ *
+ *   node_tokens, node_parents [total_q] i32; qo_indptr [bs+1] i32.
+ *   target_probs [total_q, vocab] f32: non-negative (temperature, top-k and
+ *                top-p already applied by the caller; rows need not sum to 1).
+ *   coins [total_q] f32 in [0, 1): the coin of node c, used when c is tried.
+ *   bonus_uniforms [bs] f32 in [0, 1).
+ *   outputs as ddtree_accept: accepted_nodes [bs, D+1] (-1 padded),
+ *   accept_len [bs], commit_tokens [bs, D+1] (accepted drafts then the
+ *   bonus), bonus_tokens [bs] (-1 if the residual has no mass).
+ * Errors: EINVAL (null pointer, bs < 0, depth_max < 0, vocab < 1).  A node
+ * with more than 1024 children keeps only the first 1024 rejections.
+ */
+int ddtree_tree_sample(const int32_t* node_tokens, const int32_t* node_parents,
+                       const int32_t* qo_indptr, const float* target_probs, const float* coins,
+                       const float* bonus_uniforms, int bs, int depth_max, int vocab,
+                       int32_t* accepted_nodes, int32_t* accept_len, int32_t* commit_tokens,
+                       int32_t* bonus_tokens, void* stream);
 
 /*
  * ddtree_commit_kv -- the accepted path enters each request's KV cache.

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_stages():
     names = declared_functions()
     for n in ("ddtree_build_tree", "ddtree_compile_visibility", "ddtree_verify_attn", "ddtree_accept",
-              "ddtree_commit_kv", "ddtree_drafter_topk"):
+              "ddtree_commit_kv", "ddtree_drafter_topk", "ddtree_tree_sample"):
         assert n in names
 
 
@@ -153,6 +153,21 @@ def test_drafter_topk_validation(lib):
     assert f(FAKE, F32, 4, 100, 8, FAKE, FAKE, NULL, need, NULL) == EWORKSPACE
     assert "drafter_topk" in _err(lib)
     assert f(NULL, F32, 0, 100, 8, NULL, NULL, NULL, 0, NULL) == 0
+
+
+def test_tree_sample_validation(lib):
+    f = lib.ddtree_tree_sample
+    args = [FAKE] * 6 + [1, 7, 512] + [FAKE] * 4 + [NULL]
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(6, -1) == EINVAL        # bs
+    assert call(3, NULL) == EINVAL      # target_probs
+    assert call(7, -1) == EINVAL        # depth_max
+    assert call(8, 0) == EINVAL         # vocab
+    assert "tree_sample" in _err(lib)
+    assert f(*([NULL] * 6 + [0, 7, 512] + [NULL] * 5)) == 0
 
 
 def test_binding_rejects_host_tensors():

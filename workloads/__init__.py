@@ -14,5 +14,6 @@ from .gen import (  # noqa: F401
     draw_target_predict,
     draw_drafter_topk,
     draw_drafter_logits,
+    draw_target_probs,
     sensitize_tree_columns,
 )

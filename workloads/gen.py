@@ -130,6 +130,30 @@ def draw_drafter_topk(rng: np.random.Generator, depth: int, topk: int, vocab: in
     return vals, ids.astype(np.int32)
 
 
+def draw_target_probs(seed: int, node_tokens: np.ndarray, node_parents: np.ndarray,
+                      qo_indptr: np.ndarray, vocab: int, p_child: float = 0.7) -> np.ndarray:
+    """Synthetic target distributions [total_q, vocab] fp32 for stochastic
+    acceptance: each node's row is a Dirichlet(0.3) spread over the
+    vocabulary; with probability p_child a share U(0.3, 0.9) of its mass is
+    moved onto the token of one of its children (chosen uniformly), so that
+    walks go deep.  Drawn, not computed from logits."""
+    rng = np.random.default_rng(int(seed) + 0xACCE)
+    total = int(qo_indptr[-1])
+    out = np.zeros((total, vocab), np.float32)
+    for r in range(len(qo_indptr) - 1):
+        a, b = int(qo_indptr[r]), int(qo_indptr[r + 1])
+        par = np.asarray(node_parents[a:b])
+        for i in range(b - a):
+            row = rng.dirichlet(np.full(vocab, 0.3))
+            kids = np.nonzero(par == i)[0]
+            if len(kids) and rng.random() < p_child:
+                w = rng.uniform(0.3, 0.9)
+                row = row * (1.0 - w)
+                row[int(node_tokens[a + int(kids[rng.integers(0, len(kids))])])] += w
+            out[a + i] = row.astype(np.float32)
+    return out
+
+
 def draw_drafter_logits(rng: np.random.Generator, rows: int, vocab: int, std: float = 2.0,
                         dtype: str = "f32") -> np.ndarray:
     """Raw drafter logits N(0, std) [rows, vocab]: fp32, or bf16 bits (RNE)."""
