@@ -189,6 +189,47 @@ def time_drafter_topk(wl, R: int, K: int, stream):
     return ms, rows, k, nbytes
 
 
+def time_tree_sample(st, wl, K: int, stream, vocab: int = DRAFTER_VOCAB):
+    """Average duration (ms) of ddtree_tree_sample over K calls on the step's
+    tree (drawn target rows of `vocab` tokens for every node; four rotated sets
+    of coins), the mean accepted length, and the bytes the walk needs: each
+    accepted node's target row read once."""
+    import torch
+
+    from tree_verify_mla_amd import _lib
+    from workloads import draw_target_probs
+
+    x = st.x
+    tok, par = st.node_tokens.cpu().numpy(), st.node_parents.cpu().numpy()
+    probs = torch.from_numpy(draw_target_probs(wl.seed, tok, par, wl.qo_indptr, vocab)).cuda()
+    rng = np.random.default_rng(wl.seed + 31337)
+    coins = [torch.from_numpy(rng.random(wl.total_q).astype(np.float32)).cuda() for _ in range(4)]
+    bonus_u = [torch.from_numpy(rng.random(wl.bs).astype(np.float32)).cuda() for _ in range(4)]
+    D = wl.depth
+    outs = [[torch.empty(wl.bs, D + 1, dtype=torch.int32, device="cuda"),
+             torch.empty(wl.bs, dtype=torch.int32, device="cuda"),
+             torch.empty(wl.bs, D + 1, dtype=torch.int32, device="cuda"),
+             torch.empty(wl.bs, dtype=torch.int32, device="cuda")] for _ in range(4)]
+
+    def run(i):
+        _lib.ddtree_tree_sample(st.node_tokens, st.node_parents, x.qo_indptr, probs, coins[i % 4],
+                                bonus_u[i % 4], D, *outs[i % 4], stream=stream)
+
+    for i in range(4):
+        run(i)
+    torch.cuda.synchronize()
+    alen = float(np.mean([o[1].cpu().numpy().mean() for o in outs]))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        run(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    nbytes = int(sum(o[1].cpu().numpy().sum() for o in outs) / 4 * vocab * 4)
+    return ms, alen, nbytes
+
+
 def cpu_baseline(wls, budget_s: float):
     """The CPU oracle as it stands, on whole requests of the workload (cycling
     through the rotated instances) until about budget_s seconds are used."""
@@ -318,6 +359,8 @@ def main():
     commit_m_ms = time_commit(steps, K, stream, move=True)
     # the drafter's per-depth top-k (the stage before the tree build; not part of a step)
     dk_ms, dk_rows, dk_k, dk_bytes = time_drafter_topk(wls[0], R, K, stream)
+    # stochastic acceptance along the tree (the alternative to greedy accept)
+    ts_ms, ts_alen, ts_bytes = time_tree_sample(steps[0], wls[0], K, stream)
 
     achieved = flops / (attn_ms * 1e-3) / 1e12
     traffic = measured_traffic(wls[0].name)
@@ -363,7 +406,12 @@ def main():
                       "rows": dk_rows, "vocab": DRAFTER_VOCAB, "k": dk_k, "dtype": "f32",
                       "us": round(dk_ms * 1e3, 2), "bytes": dk_bytes,
                       "GBps": round(dk_bytes / (dk_ms * 1e-3) / 1e9, 1),
-                      "hbm_frac": round(dk_bytes / (dk_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}},
+                      "hbm_frac": round(dk_bytes / (dk_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+                  "tree_sample": {
+                      "vocab": DRAFTER_VOCAB, "us": round(ts_ms * 1e3, 2),
+                      "mean_accept_len": round(ts_alen, 3), "bytes": ts_bytes,
+                      "GBps": round(ts_bytes / (ts_ms * 1e-3) / 1e9, 1),
+                      "hbm_frac": round(ts_bytes / (ts_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wls, args.cpu_seconds)

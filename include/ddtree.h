@@ -254,17 +254,25 @@ int ddtree_accept(const int32_t* node_tokens, const int32_t* node_parents,
  *                top-p already applied by the caller; rows need not sum to 1).
  *   coins [total_q] f32 in [0, 1): the coin of node c, used when c is tried.
  *   bonus_uniforms [bs] f32 in [0, 1).
+ *   total_q      rows of target_probs (= qo_indptr[bs]); sizes the launch.
  *   outputs as ddtree_accept: accepted_nodes [bs, D+1] (-1 padded),
  *   accept_len [bs], commit_tokens [bs, D+1] (accepted drafts then the
  *   bonus), bonus_tokens [bs] (-1 if the residual has no mass).
- * Errors: EINVAL (null pointer, bs < 0, depth_max < 0, vocab < 1).  A node
- * with more than 1024 children keeps only the first 1024 rejections.
+ *   workspace    device scratch of ddtree_tree_sample_workspace_size(total_q)
+ *                bytes (the block masses of every row); contents on entry
+ *                are ignored.
+ * Errors: EINVAL (null pointer, bs < 0, total_q < 0, depth_max < 0,
+ * vocab < 1), EUNSUPPORTED (vocab > 2^21), EWORKSPACE.  A request is walked
+ * over its first 4096 nodes; a node with more than 1024 children keeps only
+ * its first 1024 rejections.  Tokens outside [0, vocab) are never accepted.
  */
+size_t ddtree_tree_sample_workspace_size(int total_q);
 int ddtree_tree_sample(const int32_t* node_tokens, const int32_t* node_parents,
                        const int32_t* qo_indptr, const float* target_probs, const float* coins,
-                       const float* bonus_uniforms, int bs, int depth_max, int vocab,
+                       const float* bonus_uniforms, int bs, int total_q, int depth_max, int vocab,
                        int32_t* accepted_nodes, int32_t* accept_len, int32_t* commit_tokens,
-                       int32_t* bonus_tokens, void* stream);
+                       int32_t* bonus_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * ddtree_commit_kv -- the accepted path enters each request's KV cache.

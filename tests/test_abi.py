@@ -157,17 +157,24 @@ def test_drafter_topk_validation(lib):
 
 def test_tree_sample_validation(lib):
     f = lib.ddtree_tree_sample
-    args = [FAKE] * 6 + [1, 7, 512] + [FAKE] * 4 + [NULL]
+    ws = lib.ddtree_tree_sample_workspace_size(33)
+    assert ws == 33 * 256 * 8 and lib.ddtree_tree_sample_workspace_size(0) == 0
+    args = [FAKE] * 6 + [1, 33, 7, 512] + [FAKE] * 5 + [ws, NULL]
     def call(i, v):
         a = list(args)
         a[i] = v
         return f(*a)
     assert call(6, -1) == EINVAL        # bs
     assert call(3, NULL) == EINVAL      # target_probs
-    assert call(7, -1) == EINVAL        # depth_max
-    assert call(8, 0) == EINVAL         # vocab
+    assert call(7, -1) == EINVAL        # total_q
+    assert call(8, -1) == EINVAL        # depth_max
+    assert call(9, 0) == EINVAL         # vocab
     assert "tree_sample" in _err(lib)
-    assert f(*([NULL] * 6 + [0, 7, 512] + [NULL] * 5)) == 0
+    assert call(9, 256 * 8192 + 1) == EUNSUPPORTED
+    assert call(15, ws - 1) == EWORKSPACE
+    assert call(14, NULL) == EWORKSPACE
+    assert "workspace" in _err(lib)
+    assert f(*([NULL] * 6 + [0, 0, 7, 512] + [NULL] * 5 + [0, NULL])) == 0
 
 
 def test_binding_rejects_host_tensors():

@@ -9,7 +9,10 @@ seeded generator.  Covered: budget 0 (root only: the bonus is a plain draw
 from the root's row), ragged trees up to 65 nodes, the headline batch, a
 vocabulary whose blocks are ragged (5000 = 256 x 20 - 120), a vocabulary of
 163,840 tokens, several uniform draws per workload, and a zero row (every
-token rejected: no mass left, bonus -1).
+token rejected: no mass left, bonus -1), blocks wider than one staging
+tile (vocabulary 1,279,983: 5000 tokens a block, staged one at a time),
+a vocabulary that leaves most blocks empty (513), and a caller-provided workspace reused across
+calls.
 """
 import sys
 
@@ -32,7 +35,7 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _case(wl, vocab, draws=3, zero_root_of=None):
+def _case(wl, vocab, draws=3, zero_root_of=None, workspace=False):
     orc = OracleRun(wl)
     x = to_device(wl, "cuda")
     st = VerifyStep(x)
@@ -53,12 +56,16 @@ def _case(wl, vocab, draws=3, zero_root_of=None):
            torch.empty(bs, dtype=torch.int32, device="cuda"),
            torch.empty(bs, D + 1, dtype=torch.int32, device="cuda"),
            torch.empty(bs, dtype=torch.int32, device="cuda")]
+    ws = None
+    if workspace:   # stale contents must not matter
+        ws = torch.full((_lib.ddtree_tree_sample_workspace_size(wl.total_q),), 0x7F,
+                        dtype=torch.uint8, device="cuda")
     for d in range(draws):
         coins = rng.random(wl.total_q).astype(np.float32)
         bonus_u = rng.random(bs).astype(np.float32)
         _lib.ddtree_tree_sample(st.node_tokens, st.node_parents, x.qo_indptr, probs_d,
                                 torch.from_numpy(coins).cuda(), torch.from_numpy(bonus_u).cuda(),
-                                D, *out)
+                                D, *out, workspace=ws)
         torch.cuda.synchronize()
         ref = sample.batch(orc.tokens, orc.parents, wl.qo_indptr, probs, coins, bonus_u, D)
         for got, want in zip(out, ref):
@@ -93,3 +100,11 @@ def test_sample_all_mass_on_rejected_tokens():
     wl = make_workload(get_config(3), bs=3, heads=1, budgets=[8, 8, 8], prefixes=[5, 5, 5],
                        pool_slots=1000)
     _case(wl, 512, draws=6, zero_root_of=1)
+
+
+def test_sample_wide_and_empty_blocks():
+    _say("test_sample_wide_and_empty_blocks")
+    wl = make_workload(get_config(3), bs=2, heads=1, budgets=[8, 4], prefixes=[3, 4],
+                       pool_slots=1000)
+    _case(wl, 256 * 5000 - 17, draws=2, workspace=True)
+    _case(wl, 513, draws=3, workspace=True)   # 3 tokens a block, 171 blocks in use

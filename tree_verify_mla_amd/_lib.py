@@ -59,7 +59,9 @@ def load() -> ctypes.CDLL:
     lib.ddtree_drafter_topk.restype = I
     lib.ddtree_drafter_topk.argtypes = [P, I, I, I, I, P, P, P, SZ, P]
     lib.ddtree_tree_sample.restype = I
-    lib.ddtree_tree_sample.argtypes = [P, P, P, P, P, P, I, I, I, P, P, P, P, P]
+    lib.ddtree_tree_sample_workspace_size.restype = SZ
+    lib.ddtree_tree_sample_workspace_size.argtypes = [I]
+    lib.ddtree_tree_sample.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, P, P, P, SZ, P]
     lib.ddtree_commit_kv.restype = I
     lib.ddtree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, P, P, ctypes.c_longlong, P,
                                      ctypes.c_longlong, I, P]
@@ -203,15 +205,28 @@ def ddtree_drafter_topk(logits, topk_logprobs, topk_ids, workspace=None, stream=
         _p(workspace, None, "workspace"), ws_bytes, _stream(stream)))
 
 
+def ddtree_tree_sample_workspace_size(total_q: int) -> int:
+    return int(load().ddtree_tree_sample_workspace_size(total_q))
+
+
 def ddtree_tree_sample(node_tokens, node_parents, qo_indptr, target_probs, coins, bonus_uniforms,
                        depth_max: int, accepted_nodes, accept_len, commit_tokens, bonus_tokens,
-                       stream=None):
+                       workspace=None, stream=None):
+    """Stochastic acceptance; target_probs [total_q, vocab] f32.  A workspace
+    of ddtree_tree_sample_workspace_size(total_q) bytes is allocated here when
+    none is passed."""
     bs = qo_indptr.numel() - 1
-    vocab = target_probs.shape[1]
+    total_q, vocab = target_probs.shape
+    if workspace is None:
+        workspace = torch.empty(ddtree_tree_sample_workspace_size(total_q), dtype=torch.uint8,
+                                device=target_probs.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check("ddtree_tree_sample", load().ddtree_tree_sample(
         _p(node_tokens, torch.int32, "node_tokens"), _p(node_parents, torch.int32, "node_parents"),
         _p(qo_indptr, torch.int32, "qo_indptr"), _p(target_probs, torch.float32, "target_probs"),
         _p(coins, torch.float32, "coins"), _p(bonus_uniforms, torch.float32, "bonus_uniforms"),
-        bs, int(depth_max), int(vocab), _p(accepted_nodes, torch.int32, "accepted_nodes"),
+        bs, int(total_q), int(depth_max), int(vocab),
+        _p(accepted_nodes, torch.int32, "accepted_nodes"),
         _p(accept_len, torch.int32, "accept_len"), _p(commit_tokens, torch.int32, "commit_tokens"),
-        _p(bonus_tokens, torch.int32, "bonus_tokens"), _stream(stream)))
+        _p(bonus_tokens, torch.int32, "bonus_tokens"), _p(workspace, None, "workspace"), ws_bytes,
+        _stream(stream)))

@@ -13,41 +13,132 @@
 // at bonus_u * R.
 //
 // The comparisons decide integers, so every sum has one fixed order (fp32):
-// a row is cut into NT contiguous blocks of ceil(V / NT) tokens (thread b
-// owns block b); a block's mass is its tokens summed one by one, the row's
-// mass the block masses summed one by one, and the running mass at token j
-// the masses of the blocks before j's block summed one by one plus j's
-// block's tokens up to j.  Inverse CDF: the first block b whose running
-// mass plus its own exceeds the threshold, then the first token of b whose
-// running mass does; if rounding leaves the threshold unreached in that
-// block, its last token with mass; if no block reaches it, the row's last
-// token with mass.
+// a row is cut into NB contiguous blocks of ceil(V / NB) tokens; a block's
+// mass is its tokens summed one by one, the row's mass the block masses
+// summed one by one, and the running mass at token j the masses of the
+// blocks before j's block summed one by one plus j's block's tokens up to
+// j.  Inverse CDF: the first block b whose running mass plus its own exceeds
+// the threshold, then the first token of b whose running mass does; if
+// rounding leaves the threshold unreached in that block, its last token with
+// mass; if no block reaches it, the row's last token with mass.
 //
-// One workgroup per request; its threads sum the row blocks, thread 0 takes
-// the decisions.
+// Two kernels.  block_mass_kernel sums every block of every node's row (the
+// whole [total_q, V] tensor read once, coalesced: tiles of 64 blocks x 64
+// tokens are staged through LDS and one lane keeps each block's sequential
+// sum) into the workspace.  walk_kernel (one workgroup per request) then
+// takes the decisions from those masses and the children's probabilities,
+// and for the bonus re-sums only the blocks that hold rejected tokens and
+// scans the one block the threshold falls in.
 #include "common.h"
 
 namespace {
 
-constexpr int NT = 256;       // threads = row blocks
-constexpr int MAX_REJ = 1024; // rejected tokens remembered at one node
+constexpr int NB = 256;        // blocks per row
+constexpr int GB = 64;         // blocks per block_mass workgroup
+constexpr int KT = 64;         // tokens per block per tile
+constexpr int WT = 256;        // walk threads
+constexpr int MAXQ = 4096;     // nodes per request the walk tries
+constexpr int MAX_REJ = 1024;  // rejected tokens remembered at one node
+constexpr int STAGE = 8192;    // floats of one staged block (limits ceil(V / NB))
 
-__global__ __launch_bounds__(NT) void tree_sample_kernel(
+// ---------------------------------------------------------------------------
+// block masses: bm[row][b] = sequential sum of block b, bl[row][b] = its last
+// token with mass (-1 if none)
+__global__ __launch_bounds__(256) void block_mass_kernel(const float* __restrict__ probs, int V,
+                                                         int per, float* __restrict__ bm,
+                                                         int* __restrict__ bl) {
+  __shared__ __align__(16) float tile[GB][KT + 4];  // rows 16-byte aligned; 16 lanes cover the banks
+  const int row = blockIdx.x, b0 = blockIdx.y * GB;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const float* src = probs + (size_t)row * V;
+  static_assert(256 % KT == 0 && GB * KT % 256 == 0, "tile shape");
+  constexpr int PER_T = GB * KT / 256;  // values each thread loads per tile
+  constexpr int BSTEP = 256 / KT;       // blocks one pass of the workgroup covers
+  const int kk = t % KT, bb = t / KT;   // this thread's token and block in the tile
+  float v[PER_T];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int b = b0 + bb + BSTEP * i, k = k0 + kk;
+      const int tok = b * per + k;
+      v[i] = (k < per && tok < V) ? src[tok] : 0.f;
+    }
+  };
+  float acc = 0.f;
+  int last = -1;
+  load(0);
+  for (int k0 = 0; k0 < per; k0 += KT) {
+    __syncthreads();  // the previous tile has been summed
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) tile[bb + BSTEP * i][kk] = v[i];
+    __syncthreads();
+    if (k0 + KT < per) load(k0 + KT);  // in flight while the tile is summed
+    if (w == 0) {  // the tile's padding past the block is zero: adding it is exact
+      const int base = (b0 + lane) * per + k0;
+      const float4* tr = reinterpret_cast<const float4*>(&tile[lane][0]);
+#pragma unroll
+      for (int q = 0; q < KT / 4; ++q) {
+        const float4 x = tr[q];
+        acc = acc + x.x;
+        last = x.x > 0.f ? base + 4 * q : last;
+        acc = acc + x.y;
+        last = x.y > 0.f ? base + 4 * q + 1 : last;
+        acc = acc + x.z;
+        last = x.z > 0.f ? base + 4 * q + 2 : last;
+        acc = acc + x.w;
+        last = x.w > 0.f ? base + 4 * q + 3 : last;
+      }
+    }
+  }
+  if (w == 0) {
+    bm[(size_t)row * NB + b0 + lane] = acc;
+    bl[(size_t)row * NB + b0 + lane] = last;
+  }
+}
+
+// ---------------------------------------------------------------------------
+__device__ inline float rl(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// sequential fp32 sum of n (multiple of 4) LDS values, in order
+__device__ inline float seq_sum4(const float* p, int n) {
+  float s = 0.f;
+#pragma unroll 8
+  for (int k = 0; k < n; k += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p + k);
+    s = s + v.x;
+    s = s + v.y;
+    s = s + v.z;
+    s = s + v.w;
+  }
+  return s;
+}
+
+__global__ __launch_bounds__(WT) void walk_kernel(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
     const int32_t* __restrict__ qo, const float* __restrict__ probs,
-    const float* __restrict__ coins, const float* __restrict__ bonus_u, int D, int V,
-    int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_len,
-    int32_t* __restrict__ commit, int32_t* __restrict__ bonus_out) {
-  __shared__ float s_mass[NT];
-  __shared__ int s_last[NT];
+    const float* __restrict__ coins, const float* __restrict__ bonus_u, int total_q, int D, int V,
+    int per, const float* __restrict__ bm, const int* __restrict__ bl,
+    int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_len, int32_t* __restrict__ commit,
+    int32_t* __restrict__ bonus_out) {
+  __shared__ __align__(16) float s_bm[NB];
+  __shared__ int s_bl[NB];
+  __shared__ int s_par[MAXQ], s_tok[MAXQ];
+  __shared__ float s_coin[MAXQ], s_pc[MAXQ];
   __shared__ int s_rej[MAX_REJ];
-  __shared__ int s_nrej, s_cur, s_next, s_block, s_tok;  // written by thread 0 only
-  __shared__ float s_run, s_thr;
-  const int r = blockIdx.x, t = threadIdx.x;
-  const int a = qo[r], Q = qo[r + 1] - a;
+  __shared__ __align__(16) float s_stage[STAGE];
+  __shared__ int s_aff[NB], s_group[NB];
+  // written by one thread between barriers
+  __shared__ int s_nrej, s_cur, s_next, s_ngroup, s_block, s_first, s_tokout;
+  __shared__ float s_R, s_run;
+
+  const int r = blockIdx.x, t = threadIdx.x, lane = t & 63;
+  const int a = min(max(qo[r], 0), total_q);
+  const int Q = min(max(min(qo[r + 1], total_q) - a, 0), MAXQ);
   int32_t* nodes_r = acc_nodes + (size_t)r * (D + 1);
   int32_t* commit_r = commit + (size_t)r * (D + 1);
-  for (int i = t; i <= D; i += NT) {
+  for (int i = t; i <= D; i += WT) {
     nodes_r[i] = -1;
     commit_r[i] = -1;
   }
@@ -58,116 +149,203 @@ __global__ __launch_bounds__(NT) void tree_sample_kernel(
     }
     return;
   }
-  const int per = (V + NT - 1) / NT;
-  const int lo = min(V, t * per), hi = min(V, lo + per);
-  // residual value of token j at the current node
-  auto res_of = [&](const float* row, int j) {
-    float v = row[j];
-    for (int k = 0; k < s_nrej; ++k)
-      if (s_rej[k] == j) v = 0.f;
-    return v;
-  };
-  // this thread's block mass of the current residual row, and its last
-  // token with mass
-  auto block_mass = [&](const float* row) {
-    float m = 0.f;
-    int last = -1;
-    for (int j = lo; j < hi; ++j) {
-      const float v = res_of(row, j);
-      m = m + v;
-      if (v > 0.f) last = j;
-    }
-    s_mass[t] = m;
-    s_last[t] = last;
-  };
-
-  int cur = 0, n = 1;  // current node, path length (thread 0's; s_cur for all)
+  for (int c = t; c < Q; c += WT) {
+    s_par[c] = parents[a + c];
+    s_tok[c] = tokens[a + c];
+    s_coin[c] = coins[a + c];
+  }
+  int n = 1;  // path length (wave 0's)
   if (t == 0) {
     s_nrej = 0;
     s_cur = 0;
     nodes_r[0] = 0;
   }
   __syncthreads();
+
+  // walk: per node, everyone fetches the row's block masses and the
+  // children's probabilities; wave 0 decides, every lane holding the same
+  // values
   while (true) {
-    const float* row = probs + (size_t)(a + s_cur) * V;
-    block_mass(row);
+    const int cur = s_cur;
+    const size_t row = (size_t)(a + cur);
+    s_bm[t] = bm[row * NB + t];
+    s_bl[t] = bl[row * NB + t];
+    for (int c = 1 + t; c < Q; c += WT) {
+      if (s_par[c] == cur) {
+        const int tok = s_tok[c];
+        float p = (tok >= 0 && tok < V) ? probs[row * V + tok] : 0.f;
+        // when c is tried every earlier sibling has been rejected, so an
+        // earlier sibling with the same token has zeroed it
+        for (int c2 = 1; c2 < c; ++c2)
+          if (s_par[c2] == cur && s_tok[c2] == tok) p = 0.f;
+        s_pc[c] = p;
+      }
+    }
     __syncthreads();
-    if (t == 0) {
-      float R = 0.f;
-      for (int b = 0; b < NT; ++b) R = R + s_mass[b];
-      int next = -1;
+    if (t < 64) {
+      float R = seq_sum4(s_bm, NB);
+      int next = -1, nrej = s_nrej;
       if (n < D + 1) {
-        for (int c = 1; c < Q; ++c) {
-          if (parents[a + c] != cur) continue;
-          const int tok = tokens[a + c];
-          const float pt = (tok >= 0 && tok < V) ? res_of(row, tok) : 0.f;
-          if (coins[a + c] * R < pt) {
-            next = c;
-            break;
+        for (int base = 1; base < Q && next < 0; base += 64) {
+          const int c = base + lane;
+          const bool kid = c < Q && s_par[c] == cur;
+          const float pc = kid ? s_pc[c] : 0.f, cn = kid ? s_coin[c] : 0.f;
+          const int tk = kid ? s_tok[c] : -1;
+          unsigned long long m = __ballot(kid);
+          while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            const float pt = rl(pc, j);
+            if (rl(cn, j) * R < pt) {
+              next = base + j;
+              break;
+            }
+            R = R - pt;
+            const int tok = __builtin_amdgcn_readlane(tk, j);
+            if (tok >= 0 && tok < V && nrej < MAX_REJ) {
+              if (lane == 0) s_rej[nrej] = tok;
+              ++nrej;
+            }
           }
-          R = R - pt;
-          if (s_nrej < MAX_REJ) s_rej[s_nrej++] = tok;
         }
       }
-      s_next = next;
-      s_thr = bonus_u[r] * R;
+      if (lane == 0) {
+        s_R = R;
+        s_next = next;
+        s_nrej = nrej;
+        if (next >= 0) {
+          nodes_r[n] = next;
+          commit_r[n - 1] = s_tok[next];
+          s_cur = next;
+          s_nrej = 0;
+        }
+      }
+      if (next >= 0) ++n;
     }
     __syncthreads();
-    const int next = s_next;
-    if (next < 0) break;
-    __syncthreads();  // everyone has read s_next
-    if (t == 0) {
-      nodes_r[n] = next;
-      commit_r[n - 1] = tokens[a + next];
-      ++n;
-      cur = next;
-      s_cur = next;
-      s_nrej = 0;
+    if (s_next < 0) break;  // s_next is next written after the following barrier
+  }
+
+  // bonus at the last node (s_bm, s_bl hold its row; s_rej its rejections):
+  // re-sum the blocks that hold rejected tokens with those tokens zeroed
+  const int cur = s_cur;
+  const float* src = probs + (size_t)(a + cur) * V;
+  const int nrej = s_nrej;
+  s_aff[t] = 0;
+  if (t == 0) s_ngroup = 0;
+  __syncthreads();
+  for (int k = t; k < nrej; k += WT) s_aff[s_rej[k] / per] = 1;
+  __syncthreads();
+  if (s_aff[t]) {  // the order of the list does not matter
+    s_group[atomicAdd(&s_ngroup, 1)] = t;
+    s_bl[t] = -1;
+  }
+  __syncthreads();
+  const int naff = s_ngroup;
+  const int per4 = (per + 3) & ~3;  // staged stride, zero padded
+  const int G = STAGE / per4;       // blocks staged at once (>= 1)
+  for (int g0 = 0; g0 < naff; g0 += G) {
+    const int ng = min(G, naff - g0);
+    for (int i = t; i < ng * per4; i += WT) {
+      const int k = i % per4, tok = s_group[g0 + i / per4] * per + k;
+      s_stage[i] = (k < per && tok < V) ? src[tok] : 0.f;
     }
+    __syncthreads();
+    for (int k = t; k < nrej; k += WT) {
+      const int tok = s_rej[k];
+      for (int j = 0; j < ng; ++j)
+        if (s_group[g0 + j] == tok / per) s_stage[j * per4 + tok % per] = 0.f;
+    }
+    __syncthreads();
+    for (int i = t; i < ng * per4; i += WT)
+      if (s_stage[i] > 0.f) {
+        const int b = s_group[g0 + i / per4];
+        atomicMax(&s_bl[b], b * per + i % per4);
+      }
+    if (t < ng) s_bm[s_group[g0 + t]] = seq_sum4(s_stage + t * per4, per4);
     __syncthreads();
   }
 
-  // bonus: inverse CDF of the residual at the last node (block masses are
-  // those of the residual after the last rejections)
-  const float* row = probs + (size_t)(a + s_cur) * V;
-  block_mass(row);
-  __syncthreads();
-  if (t == 0) {
-    const float thr = s_thr;
-    float run = 0.f;
-    int blk = -1;
-    for (int b = 0; b < NT; ++b) {
-      if (run + s_mass[b] > thr) {
-        blk = b;
-        break;
+  // the block the threshold falls in: wave 0 forms the running masses in
+  // order (lane l keeps those of blocks 4l .. 4l+3), then the first block
+  // whose running mass plus its own exceeds the threshold
+  if (t < 64) {
+    const float thr = bonus_u[r] * s_R;
+    float run = 0.f, mine[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int q = 0; q < NB / 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(s_bm + 4 * q);
+      const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (q == lane) mine[e] = run;
+        run = run + x[e];
       }
-      run = run + s_mass[b];
     }
-    s_block = blk;
-    s_run = run;
-    if (blk < 0) {  // the row's last token with mass
+    int k = -1;
+#pragma unroll
+    for (int e = 3; e >= 0; --e)
+      if (mine[e] + s_bm[4 * lane + e] > thr) k = e;
+    const unsigned long long m = __ballot(k >= 0);
+    if (lane == 0) {
+      s_R = thr;
+      s_block = -1;
+    }
+    if (m) {
+      const int l0 = __builtin_ctzll(m);
+      if (lane == l0) {
+        s_block = 4 * l0 + k;
+        s_run = mine[k];
+      }
+    } else if (lane == 0) {  // the row's last token with mass
       int last = -1;
-      for (int b = 0; b < NT; ++b) last = s_last[b] >= 0 ? s_last[b] : last;
-      s_tok = last;
+      for (int b = 0; b < NB; ++b) last = s_bl[b] >= 0 ? s_bl[b] : last;
+      s_tokout = last;
     }
+    if (lane == 0) s_first = INT_MAX;
   }
   __syncthreads();
-  if (t == s_block) {
-    float acc = s_run;
-    int tok = -1;
-    for (int j = lo; j < hi; ++j) {
-      const float v = res_of(row, j);
-      acc = acc + v;
-      if (acc > s_thr) {
-        tok = j;
-        break;
+  const int blk = s_block;
+  if (blk >= 0) {
+    for (int i = t; i < per4; i += WT) {
+      const int tok = blk * per + i;
+      s_stage[i] = (i < per && tok < V) ? src[tok] : 0.f;
+    }
+    __syncthreads();
+    for (int k = t; k < nrej; k += WT) {
+      const int tok = s_rej[k];
+      if (tok / per == blk) s_stage[tok % per] = 0.f;
+    }
+    __syncthreads();
+    // running masses inside the block, in order, in place
+    if (t == 0) {
+      float acc = s_run;
+#pragma unroll 4
+      for (int k = 0; k < per4; k += 4) {
+        float4 v = *reinterpret_cast<const float4*>(s_stage + k);
+        acc = acc + v.x;
+        v.x = acc;
+        acc = acc + v.y;
+        v.y = acc;
+        acc = acc + v.z;
+        v.z = acc;
+        acc = acc + v.w;
+        v.w = acc;
+        *reinterpret_cast<float4*>(s_stage + k) = v;
       }
     }
-    s_tok = tok >= 0 ? tok : s_last[t];
+    __syncthreads();
+    const float thr = s_R;
+    for (int k = t; k < per; k += WT)
+      if (s_stage[k] > thr) {
+        atomicMin(&s_first, k);
+        break;
+      }
+    __syncthreads();
+    if (t == 0) s_tokout = s_first < per ? blk * per + s_first : s_bl[blk];
   }
-  __syncthreads();
   if (t == 0) {
-    const int bonus = s_tok;
+    const int bonus = s_tokout;
     commit_r[n - 1] = bonus;
     acc_len[r] = n;
     bonus_out[r] = bonus;
@@ -176,12 +354,17 @@ __global__ __launch_bounds__(NT) void tree_sample_kernel(
 
 }  // namespace
 
+extern "C" size_t ddtree_tree_sample_workspace_size(int total_q) {
+  return total_q > 0 ? (size_t)total_q * NB * (sizeof(float) + sizeof(int)) : 0;
+}
+
 extern "C" int ddtree_tree_sample(const int32_t* node_tokens, const int32_t* node_parents,
                                   const int32_t* qo_indptr, const float* target_probs,
                                   const float* coins, const float* bonus_uniforms, int bs,
-                                  int depth_max, int vocab, int32_t* accepted_nodes,
+                                  int total_q, int depth_max, int vocab, int32_t* accepted_nodes,
                                   int32_t* accept_len, int32_t* commit_tokens,
-                                  int32_t* bonus_tokens, void* stream) {
+                                  int32_t* bonus_tokens, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   ddtree::clear_error();
   DDTREE_REQUIRE(bs >= 0, DDTREE_EINVAL, "tree_sample: bs must be >= 0");
   if (bs == 0) return DDTREE_OK;
@@ -189,10 +372,27 @@ extern "C" int ddtree_tree_sample(const int32_t* node_tokens, const int32_t* nod
                      bonus_uniforms && accepted_nodes && accept_len && commit_tokens &&
                      bonus_tokens,
                  DDTREE_EINVAL, "tree_sample: null required pointer");
+  DDTREE_REQUIRE(total_q >= 0, DDTREE_EINVAL, "tree_sample: total_q must be >= 0");
   DDTREE_REQUIRE(depth_max >= 0, DDTREE_EINVAL, "tree_sample: depth_max must be >= 0");
   DDTREE_REQUIRE(vocab >= 1, DDTREE_EINVAL, "tree_sample: vocab must be >= 1");
-  hipLaunchKernelGGL(tree_sample_kernel, dim3(bs), dim3(NT), 0, ddtree::as_stream(stream),
-                     node_tokens, node_parents, qo_indptr, target_probs, coins, bonus_uniforms,
-                     depth_max, vocab, accepted_nodes, accept_len, commit_tokens, bonus_tokens);
+  DDTREE_REQUIRE((long long)vocab <= (long long)NB * STAGE, DDTREE_EUNSUPPORTED,
+                 "tree_sample: vocab %d above the supported %d", vocab, NB * STAGE);
+  const size_t need = ddtree_tree_sample_workspace_size(total_q);
+  DDTREE_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), DDTREE_EWORKSPACE,
+                 "tree_sample: workspace of %zu bytes needed (got %zu)", need,
+                 workspace ? workspace_bytes : (size_t)0);
+  const int per = (vocab + NB - 1) / NB;
+  float* bm = static_cast<float*>(workspace);
+  int* bl = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)total_q * NB * sizeof(float));
+  hipStream_t s = ddtree::as_stream(stream);
+  if (total_q > 0) {
+    hipLaunchKernelGGL(block_mass_kernel, dim3(total_q, NB / GB), dim3(256), 0, s, target_probs,
+                       vocab, per, bm, bl);
+    const int rc = ddtree::check_launch("tree_sample");
+    if (rc != DDTREE_OK) return rc;
+  }
+  hipLaunchKernelGGL(walk_kernel, dim3(bs), dim3(WT), 0, s, node_tokens, node_parents, qo_indptr,
+                     target_probs, coins, bonus_uniforms, total_q, depth_max, vocab, per, bm, bl,
+                     accepted_nodes, accept_len, commit_tokens, bonus_tokens);
   return ddtree::check_launch("tree_sample");
 }
