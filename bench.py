@@ -192,8 +192,8 @@ def time_drafter_topk(wl, R: int, K: int, stream):
 def time_tree_sample(st, wl, K: int, stream, vocab: int = DRAFTER_VOCAB):
     """Average duration (ms) of ddtree_tree_sample over K calls on the step's
     tree (drawn target rows of `vocab` tokens for every node; four rotated sets
-    of coins), the mean accepted length, and the bytes the walk needs: each
-    accepted node's target row read once."""
+    of coins), the mean accepted length, and the bytes: every node's target
+    row read once (the block masses of all rows are formed before the walk)."""
     import torch
 
     from tree_verify_mla_amd import _lib
@@ -226,7 +226,7 @@ def time_tree_sample(st, wl, K: int, stream, vocab: int = DRAFTER_VOCAB):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    nbytes = int(sum(o[1].cpu().numpy().sum() for o in outs) / 4 * vocab * 4)
+    nbytes = wl.total_q * vocab * 4
     return ms, alen, nbytes
 
 
