@@ -75,3 +75,23 @@ def verify_request(q_r: np.ndarray, kv_r: np.ndarray, prefix_len: int,
         nodes = np.arange(len(parents))
     nodes = np.asarray(nodes, dtype=np.int64)
     return attend(np.asarray(q_r)[nodes], kv_r, mask[nodes], scale)
+
+
+def verify_request_layers(q_layers, kv_layers, prefix_len: int, parents: np.ndarray, scale: float,
+                          nodes=None):
+    """One request over L layers: q_layers[l] [Q, H, 576], kv_layers[l]
+    [P+Q, 576] (layer l's latents gathered through the request's slot list).
+
+    "The 30-Column Mask ...", sections "The Fix: Building Combined Indices"
+    and "Layer-Invariant Slot Optimization": within a step the slot
+    positions are the same in every layer and only the stored latents
+    differ, so the mask (hence the visible columns) is built once and every
+    layer attends through it; layer l's result is the single-layer verify of
+    its own queries and latents.  Returns a list of (out, lse) per layer.
+    """
+    mask = visibility.full_mask(parents, prefix_len)
+    if nodes is None:
+        nodes = np.arange(len(parents))
+    nodes = np.asarray(nodes, dtype=np.int64)
+    return [attend(np.asarray(q)[nodes], kv, mask[nodes], scale)
+            for q, kv in zip(q_layers, kv_layers)]

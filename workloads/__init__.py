@@ -15,5 +15,6 @@ from .gen import (  # noqa: F401
     draw_drafter_topk,
     draw_drafter_logits,
     draw_target_probs,
+    draw_layer,
     sensitize_tree_columns,
 )

@@ -299,3 +299,23 @@ def sensitize_tree_columns(wl: Workload, c: float = 9.0) -> Workload:
     out.q, out.kv_pool = q, pool
     out.name = wl.name + "+sensitized"
     return out
+
+
+def draw_layer(wl: Workload, layer: int, q_std: float = 0.5, kv_std: float = 0.5) -> Workload:
+    """The same step for another layer: tree inputs, lengths, slot lists and
+    pool size unchanged; fresh seeded queries and latent rows (same
+    distributions as make_workload) in the same slots; unused rows keep the
+    fill of ``wl``'s pool."""
+    import dataclasses
+
+    rng = np.random.default_rng([int(wl.seed), 1000 + int(layer)])
+    n_used = len(wl.kv_indices)
+    q = rng.standard_normal(wl.q.shape, dtype=np.float32) * np.float32(q_std)
+    rows = rng.standard_normal((n_used, LATENT), dtype=np.float32) * np.float32(kv_std)
+    pool = wl.kv_pool.copy()
+    if wl.dtype == "bf16":
+        q = f32_to_bf16_bits(q)
+        pool[wl.kv_indices] = f32_to_bf16_bits(rows)
+    else:
+        pool[wl.kv_indices] = rows
+    return dataclasses.replace(wl, q=q, kv_pool=pool)
