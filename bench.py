@@ -230,6 +230,63 @@ def time_tree_sample(st, wl, K: int, stream, vocab: int = DRAFTER_VOCAB):
     return ms, alen, nbytes
 
 
+def time_layers(cfg_index: int, L: int, K: int, stream):
+    """ddtree_verify_attn_layers over L layers (seeded latents per layer, one
+    slot list) against L back-to-back ddtree_verify_attn calls: average ms of
+    one layered call and of the L single calls."""
+    import torch
+
+    from tree_verify_mla_amd import _lib
+    from tree_verify_mla_amd.step import VerifyStep
+    from workloads import draw_layer, get_config, make_workload
+    from workloads.device import to_device
+
+    wl0 = make_workload(get_config(cfg_index))
+    xs = [to_device(w, "cuda") for w in [wl0] + [draw_layer(wl0, l) for l in range(1, L)]]
+    st = VerifyStep(xs[0])
+    st.build(stream)
+    st.visibility(stream)
+    q = torch.stack([x.q for x in xs]).contiguous()
+    pool = torch.stack([x.kv_pool for x in xs]).contiguous()
+    del xs[1:]
+    x0 = xs[0]
+    T, H = x0.q.shape[0], x0.q.shape[1]
+    out = torch.empty(L, T, H, 512, dtype=q.dtype, device="cuda")
+    lse = torch.empty(L, T, H, dtype=torch.float32, device="cuda")
+    dt = _lib.DDTREE_BF16 if q.dtype == torch.bfloat16 else _lib.DDTREE_F32
+    ws = torch.empty(max(1, _lib.ddtree_verify_attn_layers_workspace_size(
+        L, wl0.bs, H, wl0.max_q_len, wl0.max_kv_len, 0, dt)), dtype=torch.uint8, device="cuda")
+    sc = float(np.float32(wl0.scale))
+    args = (x0.kv_indptr, x0.kv_indices, x0.qo_indptr, st.vis_bits, wl0.max_q_len, wl0.max_kv_len, sc)
+
+    def layered():
+        _lib.ddtree_verify_attn_layers(q, pool, *args, out, lse, workspace=ws, stream=stream)
+
+    def singles():
+        for l in range(L):
+            _lib.ddtree_verify_attn(q[l], pool[l], *args, out[l], lse[l], workspace=ws, stream=stream)
+
+    # warm both up together for at least 200 ms, so neither is timed at low clocks
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        layered()
+        singles()
+        torch.cuda.synchronize()
+    res = []
+    for fn in (layered, singles):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / K)
+    return {"workload": wl0.name, "layers": L, "layered_call_us": round(res[0] * 1e3, 2),
+            "single_calls_us": round(res[1] * 1e3, 2),
+            "per_layer_us": {"layered": round(res[0] * 1e3 / L, 2), "single": round(res[1] * 1e3 / L, 2)},
+            "speedup": round(res[1] / res[0], 3)}
+
+
 def cpu_baseline(wls, budget_s: float):
     """The CPU oracle as it stands, on whole requests of the workload (cycling
     through the rotated instances) until about budget_s seconds are used."""
@@ -361,6 +418,8 @@ def main():
     dk_ms, dk_rows, dk_k, dk_bytes = time_drafter_topk(wls[0], R, K, stream)
     # stochastic acceptance along the tree (the alternative to greedy accept)
     ts_ms, ts_alen, ts_bytes = time_tree_sample(steps[0], wls[0], K, stream)
+    # one launch over several layers against one launch per layer
+    layers = [time_layers(2, 16, K, stream), time_layers(3, 4, max(5, K // 5), stream)]
 
     achieved = flops / (attn_ms * 1e-3) / 1e12
     traffic = measured_traffic(wls[0].name)
@@ -411,7 +470,8 @@ def main():
                       "vocab": DRAFTER_VOCAB, "us": round(ts_ms * 1e3, 2),
                       "mean_accept_len": round(ts_alen, 3), "bytes": ts_bytes,
                       "GBps": round(ts_bytes / (ts_ms * 1e-3) / 1e9, 1),
-                      "hbm_frac": round(ts_bytes / (ts_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}},
+                      "hbm_frac": round(ts_bytes / (ts_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+                  "verify_attn_layers": layers},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wls, args.cpu_seconds)

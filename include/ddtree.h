@@ -8,6 +8,7 @@
  *   ddtree_compile_visibility  ancestor-or-self bitsets (+ positions, + dense mask)
  *   ddtree_verify_attn         absorbed-MLA attention of every tree node x head
  *                              over the shared prefix plus its own ancestors
+ *   ddtree_verify_attn_layers  (or) the same over several layers in one launch
  *   ddtree_accept              greedy walk along the target argmax
  *   ddtree_tree_sample         (or) stochastic acceptance against the target distribution
  *   ddtree_commit_kv           the accepted path into the KV cache (after accept)
@@ -197,6 +198,42 @@ int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t num_slots,
                        int bs, int num_heads, int max_q_len, int max_kv_len, float scale,
                        int dtype, void* out, float* lse, int num_splits, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * ddtree_verify_attn_layers -- ddtree_verify_attn over L layers in one
+ * launch, sharing the step's slot lists, visibility and work schedule.
+ *
+ * The slot positions of a step do not change from layer to layer, only the
+ * latents stored in them do, so the combined index list is built once per
+ * step and serves every layer ("The 30-Column Mask ...", sections "The Fix:
+ * Building Combined Indices" and "Layer-Invariant Slot Optimization").  Layer l reads q + l * q_layer_stride
+ * and kv_pool + l * kv_layer_stride and writes out + l * out_layer_stride
+ * and lse + l * lse_layer_stride (strides in elements of each array; a zero
+ * input stride shares one array across layers); every other argument and
+ * the result of each layer are exactly those of ddtree_verify_attn.  Layer
+ * outputs must not overlap.  Small layers share one launch; a layer whose
+ * work alone fills the device (bf16, automatic split, at least 64 KV blocks
+ * of 32 columns per compute unit by the host bounds) gets a launch of its
+ * own, still enqueued by this one call.  Useful where the queries of several layers are
+ * at hand together; within one forward pass layer l + 1's queries need
+ * layer l's output.
+ *   workspace  ddtree_verify_attn_layers_workspace_size() bytes: one
+ *              single-layer workspace per layer.
+ * Errors: those of ddtree_verify_attn, and EINVAL for num_layers outside
+ * [1, 65535] or a negative stride.
+ */
+size_t ddtree_verify_attn_layers_workspace_size(int num_layers, int bs, int num_heads,
+                                                int max_q_len, int max_kv_len, int num_splits,
+                                                int dtype);
+int ddtree_verify_attn_layers(int num_layers, const void* q, int64_t q_layer_stride,
+                              const void* kv_pool, int64_t kv_layer_stride, int64_t num_slots,
+                              const int32_t* kv_indptr, const int32_t* kv_indices,
+                              const int32_t* qo_indptr, const uint32_t* vis_bits,
+                              int words_per_row, int bs, int num_heads, int max_q_len,
+                              int max_kv_len, float scale, int dtype, void* out,
+                              int64_t out_layer_stride, float* lse, int64_t lse_layer_stride,
+                              int num_splits, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * ddtree_accept -- greedy acceptance along the target argmax.

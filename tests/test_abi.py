@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_stages():
     names = declared_functions()
     for n in ("ddtree_build_tree", "ddtree_compile_visibility", "ddtree_verify_attn", "ddtree_accept",
-              "ddtree_commit_kv", "ddtree_drafter_topk", "ddtree_tree_sample"):
+              "ddtree_commit_kv", "ddtree_drafter_topk", "ddtree_tree_sample",
+              "ddtree_verify_attn_layers"):
         assert n in names
 
 
@@ -182,3 +183,34 @@ def test_binding_rejects_host_tensors():
     t = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError):
         _lib.ddtree_accept(t, t, t, t, 7, t, t, t, t)
+
+
+def test_verify_attn_layers_validation(lib):
+    f = lib.ddtree_verify_attn_layers
+    F32 = _lib.DDTREE_F32
+    # L, q, q_ls, kv, kv_ls, num_slots, kvp, kvi, qo, vis, W, bs, H, max_q, max_kv, scale, dtype,
+    # out, out_ls, lse, lse_ls, splits, ws, ws_bytes, stream
+    args = [2, FAKE, 100, FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 9, 20, 0.1, F32,
+            FAKE, 100, NULL, 0, 0, NULL, 0, NULL]
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(0, 0) == EINVAL and "num_layers" in _err(lib)
+    assert call(0, 65536) == EINVAL
+    assert call(2, -1) == EINVAL and "stride" in _err(lib)
+    assert call(4, -1) == EINVAL
+    assert call(18, -5) == EINVAL
+    assert call(1, NULL) == EINVAL
+    assert call(16, 7) == EINVAL                       # dtype
+    # workspace: L single-layer workspaces
+    one = lib.ddtree_verify_attn_workspace_size(2, 8, 33, 100, 3, F32)
+    assert lib.ddtree_verify_attn_layers_workspace_size(5, 2, 8, 33, 100, 3, F32) == 5 * one
+    assert lib.ddtree_verify_attn_layers_workspace_size(0, 2, 8, 33, 100, 3, F32) == 0
+    a = list(args)
+    a[21], a[23] = 3, 2 * lib.ddtree_verify_attn_workspace_size(1, 8, 9, 20, 3, F32) - 1
+    a[22] = FAKE
+    assert f(*a) == EWORKSPACE
+    a = list(args)
+    a[11] = 0                                          # bs == 0: nothing to do
+    assert f(*a) == 0

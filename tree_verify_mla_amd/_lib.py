@@ -52,6 +52,11 @@ def load() -> ctypes.CDLL:
     lib.ddtree_verify_attn_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.ddtree_verify_attn.restype = I
     lib.ddtree_verify_attn.argtypes = [P, P, I64, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P, SZ, P]
+    lib.ddtree_verify_attn_layers_workspace_size.restype = SZ
+    lib.ddtree_verify_attn_layers_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.ddtree_verify_attn_layers.restype = I
+    lib.ddtree_verify_attn_layers.argtypes = [I, P, I64, P, I64, I64, P, P, P, P, I, I, I, I, I, F,
+                                              I, P, I64, P, I64, I, P, SZ, P]
     lib.ddtree_accept.restype = I
     lib.ddtree_accept.argtypes = [P, P, P, P, I, I, P, P, P, P, P]
     lib.ddtree_drafter_topk_workspace_size.restype = SZ
@@ -145,6 +150,43 @@ def ddtree_verify_attn(q, kv_pool, kv_indptr, kv_indices, qo_indptr, vis_bits, m
         _p(qo_indptr, torch.int32, "qo_indptr"), _p(vis_bits, torch.int32, "vis_bits"),
         vis_bits.shape[1], bs, H, int(max_q_len), int(max_kv_len), float(scale), dt,
         _p(out, q.dtype, "out"), _p(lse, torch.float32, "lse"), int(num_splits),
+        _p(workspace, None, "workspace"), ws_bytes, _stream(stream)))
+
+
+def ddtree_verify_attn_layers_workspace_size(num_layers: int, bs: int, num_heads: int,
+                                             max_q_len: int, max_kv_len: int, num_splits: int,
+                                             dtype: int) -> int:
+    return int(load().ddtree_verify_attn_layers_workspace_size(
+        num_layers, bs, num_heads, max_q_len, max_kv_len, num_splits, dtype))
+
+
+def ddtree_verify_attn_layers(q, kv_pool, kv_indptr, kv_indices, qo_indptr, vis_bits,
+                              max_q_len: int, max_kv_len: int, scale: float, out, lse=None,
+                              num_splits: int = 0, workspace=None, stream=None):
+    """q [L, total_q, H, 576], kv_pool [L, num_slots, 576] (or [1, ...]: one
+    pool for every layer), out [L, total_q, H, 512], lse None or [L, total_q, H]."""
+    if q.dtype == torch.bfloat16:
+        dt = DDTREE_BF16
+    elif q.dtype == torch.float32:
+        dt = DDTREE_F32
+    else:
+        raise TypeError("q must be bfloat16 or float32")
+    L, total_q, H, width = q.shape
+    if kv_pool.dim() != 3 or kv_pool.shape[0] not in (1, L):
+        raise ValueError("kv_pool must be [L, num_slots, 576] or [1, num_slots, 576]")
+    if out.shape[0] != L or (lse is not None and lse.shape[0] != L):
+        raise ValueError("out and lse need one entry per layer")
+    bs = qo_indptr.numel() - 1
+    kv_ls = kv_pool.stride(0) if kv_pool.shape[0] == L and L > 1 else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("ddtree_verify_attn_layers", load().ddtree_verify_attn_layers(
+        L, _p(q, q.dtype, "q"), q.stride(0), _p(kv_pool, q.dtype, "kv_pool"), kv_ls,
+        int(kv_pool.shape[1]),
+        _p(kv_indptr, torch.int32, "kv_indptr"), _p(kv_indices, torch.int32, "kv_indices"),
+        _p(qo_indptr, torch.int32, "qo_indptr"), _p(vis_bits, torch.int32, "vis_bits"),
+        vis_bits.shape[1], bs, H, int(max_q_len), int(max_kv_len), float(scale), dt,
+        _p(out, q.dtype, "out"), out.stride(0), _p(lse, torch.float32, "lse"),
+        0 if lse is None else lse.stride(0), int(num_splits),
         _p(workspace, None, "workspace"), ws_bytes, _stream(stream)))
 
 

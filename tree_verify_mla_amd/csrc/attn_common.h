@@ -58,7 +58,22 @@ struct Params {
   void* out;
   float* lse;
   float* ws;      // partial slots
+  // layer l (grid y) reads and writes these arrays advanced by l times the
+  // stride (bytes); one layer: all zero
+  long long q_lsb, pool_lsb, out_lsb, lse_lsb, ws_lsb;
+  int L;          // layers (grid y)
 };
+
+// The parameters of layer blockIdx.y.  Null lse / ws stay null.
+__device__ inline Params at_layer(Params p) {
+  const long long l = blockIdx.y;
+  p.q = static_cast<const char*>(p.q) + l * p.q_lsb;
+  p.pool = static_cast<const char*>(p.pool) + l * p.pool_lsb;
+  p.out = static_cast<char*>(p.out) + l * p.out_lsb;
+  if (p.lse) p.lse = reinterpret_cast<float*>(reinterpret_cast<char*>(p.lse) + l * p.lse_lsb);
+  if (p.ws) p.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws) + l * p.ws_lsb);
+  return p;
+}
 
 // floats per partial slot: O [mt][512], m [mt], l [mt]
 __host__ __device__ constexpr long long slot_floats(int mt) { return (long long)mt * (DV + 2); }

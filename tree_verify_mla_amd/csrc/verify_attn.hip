@@ -33,7 +33,8 @@ __device__ inline float wave_sum(float v) {
 // fp32 path: one wavefront per query row, columns one at a time.  Lane k
 // owns latent entries k + 64j (9 of the 576 for the score, 8 of the 512
 // for the output).
-__global__ __launch_bounds__(256) void attn_f32_kernel(Params p) {
+__global__ __launch_bounds__(256) void attn_f32_kernel(Params p_all) {
+  const Params p = at_layer(p_all);
   const int S = p.S;
   const int wg = blockIdx.x;
   const int s = wg % S;
@@ -143,7 +144,8 @@ __device__ inline bool merge_plan(const Params& p, int r, int t, const Geom& g, 
   return w_last != m.w_first;
 }
 
-__global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p, int mt, int G, int dtype) {
+__global__ __launch_bounds__(64 * MERGE_ROWS) void merge_kernel(Params p_all, int mt, int G, int dtype) {
+  const Params p = at_layer(p_all);
   const int groups = (mt + MERGE_ROWS - 1) / MERGE_ROWS;
   const int tile = blockIdx.x / groups, rgrp = blockIdx.x % groups;
   const int r = tile / p.T_max, t = tile % p.T_max;
@@ -253,7 +255,8 @@ __device__ inline bool merge_plan_fast(const Params& p, int r, int t, const Geom
 constexpr int LANES_BATCH = 4;
 constexpr int LANES_STR = 256 + 16;  // bytes per staged row (padded: no bank conflicts)
 
-__global__ __launch_bounds__(128) void merge_lanes_kernel(Params p, int G) {
+__global__ __launch_bounds__(128) void merge_lanes_kernel(Params p_all, int G) {
+  const Params p = at_layer(p_all);
   constexpr int mt = MT_BF16, RG = 4, FB = 4;
   typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -335,18 +338,18 @@ __global__ __launch_bounds__(128) void merge_lanes_kernel(Params p, int G) {
 }  // namespace
 
 int launch_f32(const Params& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(grid, p.L), dim3(256), 0, s, p);
   return check_launch("verify_attn(f32)");
 }
 
 int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s) {
   if (mt == MT_BF16) {  // the matrix-core kernel's lane-layout partials (bf16 output)
     const long long groups = (long long)p.bs * p.T_max * 16;
-    hipLaunchKernelGGL(merge_lanes_kernel, dim3((unsigned)groups), dim3(128), 0, s, p, grid_groups);
+    hipLaunchKernelGGL(merge_lanes_kernel, dim3((unsigned)groups, p.L), dim3(128), 0, s, p, grid_groups);
     return check_launch("verify_attn(merge)");
   }
   const long long groups = (long long)p.bs * p.T_max * ((mt + MERGE_ROWS - 1) / MERGE_ROWS);
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)groups), dim3(64 * MERGE_ROWS), 0, s, p, mt,
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)groups, p.L), dim3(64 * MERGE_ROWS), 0, s, p, mt,
                      grid_groups, dtype);
   return check_launch("verify_attn(merge)");
 }
@@ -374,41 +377,49 @@ extern "C" size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int m
   return (size_t)(slots * slot_floats(mt) * (long long)sizeof(float));
 }
 
-extern "C" int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t num_slots,
-                                  const int32_t* kv_indptr, const int32_t* kv_indices,
-                                  const int32_t* qo_indptr, const uint32_t* vis_bits,
-                                  int words_per_row, int bs, int num_heads, int max_q_len,
-                                  int max_kv_len, float scale, int dtype, void* out, float* lse,
-                                  int num_splits, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+namespace {
+
+// One call over L layers (L = 1: the single-layer entry point).  Strides are
+// in elements of the respective arrays.
+int verify_attn_impl(const char* fn, int L, const void* q, long long q_ls, const void* kv_pool,
+                     long long kv_ls, int64_t num_slots, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, const int32_t* qo_indptr, const uint32_t* vis_bits,
+                     int words_per_row, int bs, int num_heads, int max_q_len, int max_kv_len,
+                     float scale, int dtype, void* out, long long out_ls, float* lse,
+                     long long lse_ls, int num_splits, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   ddtree::clear_error();
-  DDTREE_REQUIRE(bs >= 0, DDTREE_EINVAL, "verify_attn: bs must be >= 0");
+  DDTREE_REQUIRE(L >= 1 && L <= 65535, DDTREE_EINVAL, "%s: num_layers must be in [1, 65535]", fn);
+  DDTREE_REQUIRE(bs >= 0, DDTREE_EINVAL, "%s: bs must be >= 0", fn);
   if (bs == 0) return DDTREE_OK;
   DDTREE_REQUIRE(q && kv_pool && kv_indptr && kv_indices && qo_indptr && vis_bits && out,
-                 DDTREE_EINVAL, "verify_attn: null required pointer");
-  DDTREE_REQUIRE(num_heads >= 1, DDTREE_EINVAL, "verify_attn: num_heads must be >= 1");
-  DDTREE_REQUIRE(max_q_len >= 1, DDTREE_EINVAL, "verify_attn: max_q_len must be >= 1");
+                 DDTREE_EINVAL, "%s: null required pointer", fn);
+  DDTREE_REQUIRE(q_ls >= 0 && kv_ls >= 0 && out_ls >= 0 && lse_ls >= 0, DDTREE_EINVAL,
+                 "%s: layer strides must be >= 0", fn);
+  DDTREE_REQUIRE(num_heads >= 1, DDTREE_EINVAL, "%s: num_heads must be >= 1", fn);
+  DDTREE_REQUIRE(max_q_len >= 1, DDTREE_EINVAL, "%s: max_q_len must be >= 1", fn);
   DDTREE_REQUIRE(max_kv_len >= max_q_len, DDTREE_EINVAL,
-                 "verify_attn: max_kv_len (%d) < max_q_len (%d)", max_kv_len, max_q_len);
+                 "%s: max_kv_len (%d) < max_q_len (%d)", fn, max_kv_len, max_q_len);
   DDTREE_REQUIRE((long long)words_per_row * 32 >= max_q_len, DDTREE_EINVAL,
-                 "verify_attn: words_per_row %d too small for max_q_len %d", words_per_row,
-                 max_q_len);
-  DDTREE_REQUIRE(std::isfinite(scale), DDTREE_EINVAL, "verify_attn: scale must be finite");
-  DDTREE_REQUIRE(num_slots >= 1, DDTREE_EINVAL, "verify_attn: num_slots must be >= 1");
-  DDTREE_REQUIRE(num_splits >= 0, DDTREE_EINVAL, "verify_attn: num_splits must be >= 0");
+                 "%s: words_per_row %d too small for max_q_len %d", fn, words_per_row, max_q_len);
+  DDTREE_REQUIRE(std::isfinite(scale), DDTREE_EINVAL, "%s: scale must be finite", fn);
+  DDTREE_REQUIRE(num_slots >= 1, DDTREE_EINVAL, "%s: num_slots must be >= 1", fn);
+  DDTREE_REQUIRE(num_splits >= 0, DDTREE_EINVAL, "%s: num_splits must be >= 0", fn);
   DDTREE_REQUIRE(dtype == DDTREE_F32 || dtype == DDTREE_BF16, DDTREE_EINVAL,
-                 "verify_attn: unknown dtype %d", dtype);
-  const size_t need = ddtree_verify_attn_workspace_size(bs, num_heads, max_q_len, max_kv_len,
-                                                        num_splits, dtype);
+                 "%s: unknown dtype %d", fn, dtype);
+  const size_t per_layer = ddtree_verify_attn_workspace_size(bs, num_heads, max_q_len, max_kv_len,
+                                                             num_splits, dtype);
+  const size_t need = per_layer * (size_t)L;
   DDTREE_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), DDTREE_EWORKSPACE,
-                 "verify_attn: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+                 "%s: workspace of %zu bytes given, %zu needed", fn, workspace_bytes, need);
   const int mt = dtype == DDTREE_BF16 ? MT_BF16 : MT_F32;
   const long long T_max = ((long long)max_q_len * num_heads + mt - 1) / mt;
   DDTREE_REQUIRE(T_max * bs * (num_splits > 0 ? num_splits : 1) < (1LL << 31) &&
                      T_max * bs * ((mt + MERGE_ROWS - 1) / MERGE_ROWS) < (1LL << 31) &&
                      T_max * bs * 16 < (1LL << 31),
-                 DDTREE_EUNSUPPORTED, "verify_attn: grid too large");
+                 DDTREE_EUNSUPPORTED, "%s: grid too large", fn);
 
+  const long long esz = dtype == DDTREE_BF16 ? 2 : 4;
   Params p;
   p.q = q;
   p.pool = kv_pool;
@@ -425,6 +436,12 @@ extern "C" int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t nu
   p.out = out;
   p.lse = lse;
   p.ws = static_cast<float*>(workspace);
+  p.q_lsb = q_ls * esz;
+  p.pool_lsb = kv_ls * esz;
+  p.out_lsb = out_ls * esz;
+  p.lse_lsb = lse_ls * (long long)sizeof(float);
+  p.ws_lsb = (long long)per_layer;
+  p.L = L;
   hipStream_t s = ddtree::as_stream(stream);
 
   if (dtype == DDTREE_F32) {
@@ -437,11 +454,69 @@ extern "C" int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t nu
   int G;
   if (num_splits == 0) {
     G = bf16_grid();
-    DDTREE_REQUIRE(G > 0, DDTREE_EHIP, "verify_attn: cannot query the device compute units");
+    DDTREE_REQUIRE(G > 0, DDTREE_EHIP, "%s: cannot query the device compute units", fn);
   } else {
     G = (int)(bs * T_max * num_splits);
   }
-  int rc = launch_bf16(p, G, s);
-  if (rc != DDTREE_OK || num_splits == 1) return rc;
-  return launch_merge(p, mt, G, dtype, s);
+  // Layers run side by side in one launch (grid y) when a layer's work is
+  // small; when it already gives every workgroup of the persistent grid a
+  // long range (at least LAYER_ALONE_UNITS units, bounded from the host
+  // sizes), one launch per layer keeps each layer's working set alone in
+  // the caches, which measured faster.
+  constexpr long long LAYER_ALONE_UNITS = 64;
+  const long long units_bound = (long long)bs * T_max * ((max_kv_len + KB - 1) / KB);
+  const bool one_by_one = L > 1 && num_splits == 0 && units_bound >= LAYER_ALONE_UNITS * G;
+  for (int l = 0; l < (one_by_one ? L : 1); ++l) {
+    Params pl = p;
+    if (one_by_one) {
+      pl.L = 1;
+      pl.q = static_cast<const char*>(p.q) + l * p.q_lsb;
+      pl.pool = static_cast<const char*>(p.pool) + l * p.pool_lsb;
+      pl.out = static_cast<char*>(p.out) + l * p.out_lsb;
+      if (p.lse) pl.lse = reinterpret_cast<float*>(reinterpret_cast<char*>(p.lse) + l * p.lse_lsb);
+      if (p.ws) pl.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws) + l * p.ws_lsb);
+    }
+    int rc = launch_bf16(pl, G, s);
+    if (rc == DDTREE_OK && num_splits != 1) rc = launch_merge(pl, mt, G, dtype, s);
+    if (rc != DDTREE_OK) return rc;
+  }
+  return DDTREE_OK;
+}
+
+}  // namespace
+
+extern "C" int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t num_slots,
+                                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* qo_indptr, const uint32_t* vis_bits,
+                                  int words_per_row, int bs, int num_heads, int max_q_len,
+                                  int max_kv_len, float scale, int dtype, void* out, float* lse,
+                                  int num_splits, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return verify_attn_impl("verify_attn", 1, q, 0, kv_pool, 0, num_slots, kv_indptr, kv_indices,
+                          qo_indptr, vis_bits, words_per_row, bs, num_heads, max_q_len, max_kv_len,
+                          scale, dtype, out, 0, lse, 0, num_splits, workspace, workspace_bytes,
+                          stream);
+}
+
+extern "C" size_t ddtree_verify_attn_layers_workspace_size(int num_layers, int bs, int num_heads,
+                                                           int max_q_len, int max_kv_len,
+                                                           int num_splits, int dtype) {
+  if (num_layers < 1) return 0;
+  return ddtree_verify_attn_workspace_size(bs, num_heads, max_q_len, max_kv_len, num_splits,
+                                           dtype) *
+         (size_t)num_layers;
+}
+
+extern "C" int ddtree_verify_attn_layers(
+    int num_layers, const void* q, int64_t q_layer_stride, const void* kv_pool,
+    int64_t kv_layer_stride, int64_t num_slots, const int32_t* kv_indptr,
+    const int32_t* kv_indices, const int32_t* qo_indptr, const uint32_t* vis_bits,
+    int words_per_row, int bs, int num_heads, int max_q_len, int max_kv_len, float scale,
+    int dtype, void* out, int64_t out_layer_stride, float* lse, int64_t lse_layer_stride,
+    int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_attn_impl("verify_attn_layers", num_layers, q, q_layer_stride, kv_pool,
+                          kv_layer_stride, num_slots, kv_indptr, kv_indices, qo_indptr, vis_bits,
+                          words_per_row, bs, num_heads, max_q_len, max_kv_len, scale, dtype, out,
+                          out_layer_stride, lse, lse_layer_stride, num_splits, workspace,
+                          workspace_bytes, stream);
 }

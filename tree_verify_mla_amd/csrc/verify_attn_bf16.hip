@@ -195,10 +195,11 @@ __device__ inline float other_half(float x) {
 // form for larger pools) every LDS read waits for all outstanding LDS
 // traffic.
 template <bool BUF>
-__global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
+__global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
   // The body uses buffer-resource builtins that exist only for the device;
   // the host pass needs nothing but the kernel's symbol.
 #if defined(__HIP_DEVICE_COMPILE__)
+  const Params p = at_layer(p_all);
   constexpr int MT = 32 * NWAVE;
   static_assert(MT == MT_BF16, "tile rows must match the schedule");
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -799,9 +800,9 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p) {
 
 int launch_bf16(const Params& p, int grid, hipStream_t s) {
   if (p.num_slots * (long long)ROWB <= 0xffffffffLL)
-    hipLaunchKernelGGL((attn_bf16_kernel<true>), dim3(grid), dim3(NWAVE * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<true>), dim3(grid, p.L), dim3(NWAVE * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<false>), dim3(grid), dim3(NWAVE * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<false>), dim3(grid, p.L), dim3(NWAVE * 64), 0, s, p);
   return check_launch("verify_attn(bf16)");
 }
 
