@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the verify step (no commit, drafter top-k, tree sampling or "
+                         "layer-batched lines), e.g. for a trace of the step's kernels alone")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -407,19 +410,41 @@ def main():
     attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     acc_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
 
-    # the KV commit after acceptance (not part of a step): index form, then
-    # the move form, last, since it compacts the instances' pools in place
-    alens = [st.accept_len.cpu().numpy() for st in steps]
-    cb_i = sum(commit_bytes(wls[k], alens[k], False) for k in range(R)) / R
-    cb_m = sum(commit_bytes(wls[k], alens[k], True) for k in range(R)) / R
-    commit_i_ms = time_commit(steps, K, stream, move=False)
-    commit_m_ms = time_commit(steps, K, stream, move=True)
-    # the drafter's per-depth top-k (the stage before the tree build; not part of a step)
-    dk_ms, dk_rows, dk_k, dk_bytes = time_drafter_topk(wls[0], R, K, stream)
-    # stochastic acceptance along the tree (the alternative to greedy accept)
-    ts_ms, ts_alen, ts_bytes = time_tree_sample(steps[0], wls[0], K, stream)
-    # one launch over several layers against one launch per layer
-    layers = [time_layers(2, 16, K, stream), time_layers(3, 4, max(5, K // 5), stream)]
+    extras = None
+    if not args.no_extras:
+        # the KV commit after acceptance (not part of a step): index form, then
+        # the move form, last, since it compacts the instances' pools in place
+        alens = [st.accept_len.cpu().numpy() for st in steps]
+        cb_i = sum(commit_bytes(wls[k], alens[k], False) for k in range(R)) / R
+        cb_m = sum(commit_bytes(wls[k], alens[k], True) for k in range(R)) / R
+        commit_i_ms = time_commit(steps, K, stream, move=False)
+        commit_m_ms = time_commit(steps, K, stream, move=True)
+        # the drafter's per-depth top-k (the stage before the tree build; not part of a step)
+        dk_ms, dk_rows, dk_k, dk_bytes = time_drafter_topk(wls[0], R, K, stream)
+        # stochastic acceptance along the tree (the alternative to greedy accept)
+        ts_ms, ts_alen, ts_bytes = time_tree_sample(steps[0], wls[0], K, stream)
+        # one launch over several layers against one launch per layer
+        layers = [time_layers(2, 16, K, stream), time_layers(3, 4, max(5, K // 5), stream)]
+        extras = {
+              "commit_kv": {
+                  "index_form_us": round(commit_i_ms * 1e3, 2),
+                  "index_form_bytes": round(cb_i),
+                  "index_form_GBps": round(cb_i / (commit_i_ms * 1e-3) / 1e9, 1),
+                  "move_form_us": round(commit_m_ms * 1e3, 2),
+                  "move_form_bytes": round(cb_m),
+                  "move_form_GBps": round(cb_m / (commit_m_ms * 1e-3) / 1e9, 1),
+                  "hbm_peak_GBps": PEAK_HBM_GBPS},
+              "drafter_topk": {
+                  "rows": dk_rows, "vocab": DRAFTER_VOCAB, "k": dk_k, "dtype": "f32",
+                  "us": round(dk_ms * 1e3, 2), "bytes": dk_bytes,
+                  "GBps": round(dk_bytes / (dk_ms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(dk_bytes / (dk_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+              "tree_sample": {
+                  "vocab": DRAFTER_VOCAB, "us": round(ts_ms * 1e3, 2),
+                  "mean_accept_len": round(ts_alen, 3), "bytes": ts_bytes,
+                  "GBps": round(ts_bytes / (ts_ms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(ts_bytes / (ts_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+              "verify_attn_layers": layers}
 
     achieved = flops / (attn_ms * 1e-3) / 1e12
     traffic = measured_traffic(wls[0].name)
@@ -453,25 +478,7 @@ def main():
                   "accept_ms": round(acc_ms, 5),
                   "attn_GBps": round(gbps, 1), "attn_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
                   "tree_steps_per_s": round(wls[0].bs / (step_ms * 1e-3), 1),
-                  "commit_kv": {
-                      "index_form_us": round(commit_i_ms * 1e3, 2),
-                      "index_form_bytes": round(cb_i),
-                      "index_form_GBps": round(cb_i / (commit_i_ms * 1e-3) / 1e9, 1),
-                      "move_form_us": round(commit_m_ms * 1e3, 2),
-                      "move_form_bytes": round(cb_m),
-                      "move_form_GBps": round(cb_m / (commit_m_ms * 1e-3) / 1e9, 1),
-                      "hbm_peak_GBps": PEAK_HBM_GBPS},
-                  "drafter_topk": {
-                      "rows": dk_rows, "vocab": DRAFTER_VOCAB, "k": dk_k, "dtype": "f32",
-                      "us": round(dk_ms * 1e3, 2), "bytes": dk_bytes,
-                      "GBps": round(dk_bytes / (dk_ms * 1e-3) / 1e9, 1),
-                      "hbm_frac": round(dk_bytes / (dk_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
-                  "tree_sample": {
-                      "vocab": DRAFTER_VOCAB, "us": round(ts_ms * 1e3, 2),
-                      "mean_accept_len": round(ts_alen, 3), "bytes": ts_bytes,
-                      "GBps": round(ts_bytes / (ts_ms * 1e-3) / 1e9, 1),
-                      "hbm_frac": round(ts_bytes / (ts_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
-                  "verify_attn_layers": layers},
+                  **(extras or {})},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wls, args.cpu_seconds)
