@@ -331,7 +331,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the verify path is built and timed on a single MI355X; "
-              "run it with --gpus 1 (multi-GPU sharding is described in DESIGN.md, not built).",
+              "run it with --gpus 1 (sharding across GPUs is not built).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -20,7 +20,7 @@ Sources:
   committed, so the cache grows by accept_len; autoregressive decoding is
   the budget-0 tree with accept_len = 1.
 
-Readings (DESIGN.md): accept_len counts the root; commit tokens are the
+Readings: accept_len counts the root; commit tokens are the
 accepted draft tokens followed by the bonus (accept_len tokens in all); if
 two children of one node carried the same token the lower node index wins;
 the walk stops after ``depth_max + 1`` path nodes.

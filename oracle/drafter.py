@@ -8,7 +8,7 @@ per depth position, and from each the vocabulary head gives the top-k
 candidate tokens with their log-probabilities; the best-first builder
 consumes them.
 
-Readings (DESIGN.md): the log-probability is the log-softmax over the whole
+Readings: the log-probability is the log-softmax over the whole
 vocabulary, computed here in fp64 from the exactly widened inputs; the top-k
 are the k largest log-probabilities in descending order, equal values in
 ascending token id; the values are returned rounded to fp32.  Since the

@@ -8,7 +8,7 @@ is walked by tree-structured rejection sampling against the target's
 (temperature-, top-k-, top-p-filtered) distribution at every node, the
 draft being the tree's tokens themselves (no draft distribution).
 
-Reading, the standard speculative-sampling rule for a
+Reading: the standard speculative-sampling rule for a
 deterministic draft, walked from the root:
 
 * at node ``cur`` the residual distribution starts as the target row

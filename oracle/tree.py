@@ -15,7 +15,7 @@ Design": the root node carries the last verified token; section "The Context:
 A Native DDTree Engine Built from Scratch": the reference builder was a
 per-request CPU heapq.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
 
 * depth d = 1..D uses top-k list d-1; D = block_size - 1 = 7;
 * scores are fp32, accumulated root-to-leaf as ``f32(parent + lp)``; a

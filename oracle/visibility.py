@@ -21,7 +21,7 @@ Sources:
   row stride is prefix_len + q_len (9 x 30 = 270 for prefix 21).
 
 Reading where the final-scheme formula was lost: full mask row i =
-``[1] * P ++ vis[i]`` with kv_len = P + q_len (listed in DESIGN.md).
+``[1] * P ++ vis[i]`` with kv_len = P + q_len.
 """
 from __future__ import annotations
 
