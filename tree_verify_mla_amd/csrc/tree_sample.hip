@@ -10,9 +10,11 @@
 // accepted iff coin[c] * R < res[t], otherwise R -= res[t] and res[t] = 0;
 // the walk stops when no child is accepted or after depth_max + 1 nodes,
 // and the bonus is drawn from the residual at the last node by inverse CDF
-// at bonus_u * R.
+// at bonus_u times the residual's mass.  A token without mass is never
+// accepted and never drawn.
 //
-// The comparisons decide integers, so every sum has one fixed order (fp32):
+// The comparisons decide integers; fp32 with one fixed order for every sum,
+// so the kernel's own results do not depend on timing:
 // a row is cut into NB contiguous blocks of ceil(V / NB) tokens; a block's
 // mass is its tokens summed one by one, the row's mass the block masses
 // summed one by one, and the running mass at token j the masses of the
@@ -196,11 +198,14 @@ __global__ __launch_bounds__(WT) void walk_kernel(
             const int j = __builtin_ctzll(m);
             m &= m - 1;
             const float pt = rl(pc, j);
-            if (rl(cn, j) * R < pt) {
+            // a token without mass is never accepted (coin * R >= 0 in exact
+            // arithmetic), nor is a running mass that rounding took below
+            // zero allowed to accept one
+            if (pt > 0.f && rl(cn, j) * R < pt) {
               next = base + j;
               break;
             }
-            R = R - pt;
+            R = fmaxf(R - pt, 0.f);
             const int tok = __builtin_amdgcn_readlane(tk, j);
             if (tok >= 0 && tok < V && nrej < MAX_REJ) {
               if (lane == 0) s_rej[nrej] = tok;
@@ -267,10 +272,10 @@ __global__ __launch_bounds__(WT) void walk_kernel(
   }
 
   // the block the threshold falls in: wave 0 forms the running masses in
-  // order (lane l keeps those of blocks 4l .. 4l+3), then the first block
-  // whose running mass plus its own exceeds the threshold
+  // order (lane l keeps those of blocks 4l .. 4l+3); the threshold is the
+  // uniform times the residual's mass in the same order (its last running
+  // mass); then the first block whose running mass plus its own exceeds it
   if (t < 64) {
-    const float thr = bonus_u[r] * s_R;
     float run = 0.f, mine[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int q = 0; q < NB / 4; ++q) {
@@ -282,6 +287,7 @@ __global__ __launch_bounds__(WT) void walk_kernel(
         run = run + x[e];
       }
     }
+    const float thr = bonus_u[r] * run;
     int k = -1;
 #pragma unroll
     for (int e = 3; e >= 0; --e)
