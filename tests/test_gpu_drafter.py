@@ -8,7 +8,9 @@ difference).  Covered: fp32 and bf16 logits, 16-byte and scalar load paths
 (vocabulary sizes that are and are not multiples of 4 / 8, and a
 misaligned row start), one chunk, many chunks and a ragged last chunk, k from
 1 to 32, a vocabulary of one token, rows of many equal logits (ties ordered
-by token id) and rows with -inf entries; full size: 56 rows (8 requests x 7
+by token id), rows with -inf entries, and rows whose last one or two
+8192-logit chunks are entirely -inf (a masked vocabulary tail: such a chunk
+has no mass and must not poison the row's log-sum-exp); full size: 56 rows (8 requests x 7
 depths) of 163,840 logits, the measured configuration.
 """
 import sys
@@ -86,6 +88,26 @@ def test_ties_and_minus_infinity():
         x[1, rng.choice(vocab, vocab // 2, replace=False)] = -np.inf
         x[2, :] = 0.0                                                   # a row of equal logits
         _check(x, torch.from_numpy(x).cuda(), 16)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_masked_tail_chunks(dtype):
+    _say(f"test_masked_tail_chunks {dtype}")
+    rng = np.random.default_rng(14)
+    vocab = 8192 * 4 + 100                         # five chunks, the last one ragged
+    x = draw_drafter_logits(rng, 4, vocab, dtype="f32")
+    x[0, 8192 * 4:] = -np.inf                      # the ragged last chunk
+    x[1, 8192 * 3:] = -np.inf                      # the last two chunks
+    x[2, :8192] = -np.inf                          # the first chunk
+    x[3, 8192:8192 * 2] = -np.inf                  # a middle chunk
+    x[3, 8192 * 4:] = -np.inf
+    if dtype == "bf16":
+        from workloads import f32_to_bf16_bits
+        xb = f32_to_bf16_bits(x)
+        xf = bf16_bits_to_f32(xb)
+        _check(xf, _dev(xb, dtype), 16)
+    else:
+        _check(x, _dev(x, dtype), 16)
 
 
 def test_full_size_headline_rows():

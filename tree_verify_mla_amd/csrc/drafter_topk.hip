@@ -147,10 +147,14 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
   __syncthreads();
   m = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
   __syncthreads();
+  // A chunk of nothing but -inf (a masked tail of the vocabulary) has no
+  // mass: its sum is 0 and its max stays -inf, which the merge skips.  The
+  // reference then is 0, so e^(-inf - 0) = 0 rather than e^(-inf + inf).
+  const float mref = m == -INFINITY ? 0.f : m;
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < EPT; ++j)
-    if ((live >> j) & 1u) s += __expf(x[j] - m);
+    if ((live >> j) & 1u) s += __expf(x[j] - mref);
   s = wave_sum_f(s);
   if (lane == 0) red_f[wave] = s;
   __syncthreads();
@@ -285,7 +289,9 @@ __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __
   float S = 0.f;
   for (int c0 = 0; c0 < C; c0 += 64) {
     const int c = c0 + lane;
-    S += wave_sum_f(c < C ? ms[2 * c + 1] * __expf(ms[2 * c] - M) : 0.f);
+    // chunks without mass (max -inf) add nothing; the row needs at least one
+    // finite logit (M finite)
+    S += wave_sum_f(c < C && ms[2 * c] != -INFINITY ? ms[2 * c + 1] * __expf(ms[2 * c] - M) : 0.f);
   }
   const float lse = M + __logf(S);
 
