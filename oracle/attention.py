@@ -49,16 +49,17 @@ def attend(q: np.ndarray, kv: np.ndarray, mask: np.ndarray, scale: float):
     n, H, _ = q.shape
     out = np.zeros((n, H, DL), dtype=np.float64)
     lse = np.zeros((n, H), dtype=np.float64)
+    v = kv[:, :DL]
     for i in range(n):
-        cols = np.nonzero(mask[i])[0]
-        if cols.size == 0:
+        if not mask[i].any():
             raise ValueError(f"query node {i} sees no column")
-        k = kv[cols]                       # [c, 576]
-        s = float(scale) * (q[i] @ k.T)    # [H, c]
+        # scores of every column; an invisible column's score is -inf, so its
+        # softmax weight is exactly 0
+        s = np.where(mask[i][None, :], float(scale) * (q[i] @ kv.T), -np.inf)   # [H, m]
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         l = e.sum(axis=1, keepdims=True)
-        out[i] = (e @ k[:, :DL]) / l
+        out[i] = (e @ v) / l
         lse[i] = (m + np.log(l))[:, 0]
     return out, lse
 

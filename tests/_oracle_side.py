@@ -39,7 +39,3 @@ class OracleRun:
         return attention.verify_request(q, kv, int(wl.prefix_lens[r]), self.parents[a:b],
                                         float(np.float32(wl.scale)), nodes=nodes)
 
-
-def sample_nodes(q_len: int) -> list:
-    """Deterministic sample: root, a middle node, the last node (deduplicated)."""
-    return sorted({0, q_len // 2, q_len - 1})

@@ -2,14 +2,15 @@
 
 Bars: tree, visibility, positions, dense mask and accept bit-exact;
 attention max|err| <= 1e-2 * max|out| for bf16 and <= 1e-5 * max|out| for
-fp32; lse within 2e-3 (bf16) / 1e-5 (fp32) absolute.  Small workloads are
-compared on every output; the full-size configurations run in the bench's
-launch configuration (persistent split, num_splits = 0) and are compared on
-sampled nodes (root, middle, last of each request, all heads).  Long-context
-configurations are also run on their sensitized twin, where a mask error
-would exceed the tolerance (tests/test_oracle_attention.py shows a leak is
-invisible at 131k prefix otherwise).  Unused pool rows are NaN, so a stray
-read poisons the output.
+fp32; lse within 2e-3 (bf16) / 1e-5 (fp32) absolute.  Every output row is
+compared at every configuration, the full-size ones included, in the
+bench's launch configuration (persistent split, num_splits = 0), so every
+split tile's log-sum-exp merge is checked.  The full-size configurations
+also run on their sensitized twin, where a mask error would exceed the
+tolerance (tests/test_oracle_attention.py shows a leak is invisible at 131k
+prefix otherwise).  Unused pool rows are NaN, so a stray read poisons the
+output.  The whole step is also captured in a HIP graph and replayed, on the
+8-head shard and on the ragged 32-request batch.
 """
 import sys
 
@@ -17,7 +18,9 @@ import numpy as np
 import pytest
 import torch
 
-from tests._oracle_side import OracleRun, sample_nodes
+import functools
+
+from tests._oracle_side import OracleRun
 from tree_verify_mla_amd import _lib
 from tree_verify_mla_amd.step import VerifyStep
 from workloads import get_config, make_workload, sensitize_tree_columns
@@ -61,23 +64,31 @@ def _check_integer_stages(orc, st):
     assert np.array_equal(st.bonus_tokens.cpu().numpy(), bonus)
 
 
-def _check_attention(orc, st, sampled: bool):
+def _check_attention(orc, st):
+    """Every output row and lse of every request against the fp64 oracle."""
     wl = orc.wl
     out = _out_f64(st)
     lse = st.lse.cpu().numpy().astype(np.float64)
     worst, worst_lse = 0.0, 0.0
     for r in range(wl.bs):
         a, b = int(wl.qo_indptr[r]), int(wl.qo_indptr[r + 1])
-        nodes = sample_nodes(b - a) if sampled else list(range(b - a))
-        ref, ref_lse = orc.attention_rows(r, nodes)
-        got = out[a + np.array(nodes)]
+        ref, ref_lse = orc.attention_rows(r)
+        got = out[a:b]
         assert np.isfinite(got).all(), f"request {r}: non-finite output"
         err = np.abs(got - ref).max() / np.abs(ref).max()
         worst = max(worst, err)
-        worst_lse = max(worst_lse, np.abs(lse[a + np.array(nodes)] - ref_lse).max())
-    _say(f"  {wl.name}: max|err|/max|out| = {worst:.3e}, max|lse err| = {worst_lse:.3e}")
+        worst_lse = max(worst_lse, np.abs(lse[a:b] - ref_lse).max())
+    _say(f"  {wl.name}: max|err|/max|out| = {worst:.3e}, max|lse err| = {worst_lse:.3e} "
+         f"over {wl.total_q} nodes x {wl.heads} heads")
     assert worst <= TOL[wl.dtype]
     assert worst_lse <= LSE_TOL[wl.dtype]
+
+
+@functools.lru_cache(maxsize=2)
+def _full_size(index: int, twin: bool):
+    """The full-size workload of a configuration (drawn once per process)."""
+    wl = make_workload(get_config(index))
+    return sensitize_tree_columns(wl) if twin else wl
 
 
 # ---------------------------------------------------------------------------
@@ -86,7 +97,7 @@ def test_c1_tiny_fp32(num_splits):
     _say(f"test_c1_tiny_fp32 splits={num_splits}")
     orc, st = _run(make_workload(get_config(1)), num_splits)
     _check_integer_stages(orc, st)
-    _check_attention(orc, st, sampled=False)
+    _check_attention(orc, st)
 
 
 @pytest.mark.parametrize("num_splits", [0, 1, 2])
@@ -94,7 +105,7 @@ def test_c1_shape_bf16(num_splits):
     _say(f"test_c1_shape_bf16 splits={num_splits}")
     orc, st = _run(make_workload(get_config(1), dtype="bf16"), num_splits)
     _check_integer_stages(orc, st)
-    _check_attention(orc, st, sampled=False)
+    _check_attention(orc, st)
 
 
 @pytest.mark.parametrize("num_splits", [0, 1, 2, 7])
@@ -102,7 +113,7 @@ def test_c2_shard_bf16_full_compare(num_splits):
     _say(f"test_c2 splits={num_splits}")
     orc, st = _run(make_workload(get_config(2)), num_splits)
     _check_integer_stages(orc, st)
-    _check_attention(orc, st, sampled=False)
+    _check_attention(orc, st)
 
 
 def test_ragged_edges_bf16():
@@ -112,10 +123,10 @@ def test_ragged_edges_bf16():
                        prefixes=[0, 1, 31, 33, 700, 5000], pool_slots=20000)
     orc, st = _run(wl)
     _check_integer_stages(orc, st)
-    _check_attention(orc, st, sampled=False)
+    _check_attention(orc, st)
     for S in (1, 5):
         orc2, st2 = _run(wl, S)
-        _check_attention(orc2, st2, sampled=False)
+        _check_attention(orc2, st2)
 
 
 def test_ragged_edges_fp32():
@@ -124,44 +135,38 @@ def test_ragged_edges_fp32():
                        pool_slots=400)
     orc, st = _run(wl)
     _check_integer_stages(orc, st)
-    _check_attention(orc, st, sampled=False)
-
-
-def test_c3_headline_full_size_sampled():
-    _say("test_c3_headline_full_size_sampled")
-    orc, st = _run(make_workload(get_config(3)))
-    _check_integer_stages(orc, st)
-    _check_attention(orc, st, sampled=True)
+    _check_attention(orc, st)
 
 
 @pytest.mark.parametrize("twin", [False, True])
-def test_c4_long_context_sampled(twin):
-    _say(f"test_c4_long_context_sampled twin={twin}")
-    wl = make_workload(get_config(4))
-    if twin:
-        wl = sensitize_tree_columns(wl)
-    orc, st = _run(wl)
+def test_c3_headline_full_size(twin):
+    _say(f"test_c3_headline_full_size twin={twin}")
+    orc, st = _run(_full_size(3, twin))
     _check_integer_stages(orc, st)
-    _check_attention(orc, st, sampled=True)
+    _check_attention(orc, st)
+
+
+@pytest.mark.parametrize("twin", [False, True])
+def test_c4_long_context_full_size(twin):
+    _say(f"test_c4_long_context_full_size twin={twin}")
+    orc, st = _run(_full_size(4, twin))
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st)
 
 
 def test_c4_forced_splits_agree():
     """Split count must not change the result beyond rounding."""
     _say("test_c4_forced_splits_agree")
-    wl = sensitize_tree_columns(make_workload(get_config(4)))
-    orc, st = _run(wl, num_splits=64)
-    _check_attention(orc, st, sampled=True)
+    orc, st = _run(_full_size(4, True), num_splits=64)
+    _check_attention(orc, st)
 
 
 @pytest.mark.parametrize("twin", [False, True])
-def test_c5_ragged_e2e_sampled(twin):
-    _say(f"test_c5_ragged_e2e_sampled twin={twin}")
-    wl = make_workload(get_config(5))
-    if twin:
-        wl = sensitize_tree_columns(wl)
-    orc, st = _run(wl)
+def test_c5_ragged_e2e_full_size(twin):
+    _say(f"test_c5_ragged_e2e_full_size twin={twin}")
+    orc, st = _run(_full_size(5, twin))
     _check_integer_stages(orc, st)
-    _check_attention(orc, st, sampled=True)
+    _check_attention(orc, st)
 
 
 def test_dense_mask_matches_oracle():
@@ -237,16 +242,16 @@ def test_accept_sentinel_and_full_chain():
     assert st.bonus_tokens.cpu().numpy().tolist() == [-1, 4242]
 
 
-def test_graph_replay_matches_eager():
-    """The whole step captured in one graph, replayed with eager work between."""
-    _say("test_graph_replay_matches_eager")
-    wl = make_workload(get_config(2))
+def _graph_replay(wl):
+    """The whole step captured in one graph, replayed with eager work between
+    the replays; every replay must equal the eager run bit for bit."""
     orc = OracleRun(wl)
     x = to_device(wl, "cuda", target_predict=orc.target_predict)
     st = VerifyStep(x)
     st.run()
     torch.cuda.synchronize()
-    eager = [t.clone() for t in (st.node_tokens, st.vis_bits, st.out, st.lse, st.commit_tokens)]
+    outs = (st.node_tokens, st.vis_bits, st.out, st.lse, st.accept_len, st.commit_tokens)
+    eager = [t.clone() for t in outs]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -257,11 +262,26 @@ def test_graph_replay_matches_eager():
     with torch.cuda.graph(g, stream=s):
         st.run(stream=s)
     for rep in range(4):
-        for t in (st.node_tokens, st.vis_bits, st.out, st.lse, st.commit_tokens):
+        for t in outs:
             t.zero_()
         junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
         g.replay()
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
-        for a, b in zip(eager, (st.node_tokens, st.vis_bits, st.out, st.lse, st.commit_tokens)):
+        for a, b in zip(eager, outs):
             assert torch.equal(a, b), f"replay {rep} differs from eager"
+    return orc, st
+
+
+def test_graph_replay_matches_eager():
+    _say("test_graph_replay_matches_eager")
+    _graph_replay(make_workload(get_config(2)))
+
+
+def test_graph_replay_ragged_batch():
+    """The ragged 32-request batch (budgets 16/32/64, prefixes 1k-32k) under
+    capture: replays equal the eager run, and the replayed step is oracle-exact
+    on the integer stages."""
+    _say("test_graph_replay_ragged_batch")
+    orc, st = _graph_replay(_full_size(5, False))
+    _check_integer_stages(orc, st)
