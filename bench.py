@@ -214,9 +214,12 @@ def time_tree_sample(st, wl, K: int, stream, vocab: int = DRAFTER_VOCAB):
              torch.empty(wl.bs, D + 1, dtype=torch.int32, device="cuda"),
              torch.empty(wl.bs, dtype=torch.int32, device="cuda")] for _ in range(4)]
 
+    ws = torch.empty(_lib.ddtree_tree_sample_workspace_size(wl.total_q), dtype=torch.uint8,
+                     device="cuda")
+
     def run(i):
         _lib.ddtree_tree_sample(st.node_tokens, st.node_parents, x.qo_indptr, probs, coins[i % 4],
-                                bonus_u[i % 4], D, *outs[i % 4], stream=stream)
+                                bonus_u[i % 4], D, *outs[i % 4], workspace=ws, stream=stream)
 
     for i in range(4):
         run(i)

@@ -12,6 +12,7 @@
  *   ddtree_accept              greedy walk along the target argmax
  *   ddtree_tree_sample         (or) stochastic acceptance against the target distribution
  *   ddtree_commit_kv           the accepted path into the KV cache (after accept)
+ *   ddtree_validate_inputs     (debug) checks the index arrays a step is built from
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -93,7 +94,8 @@ const char* ddtree_last_error(void);
  * lexicographically smaller rank path.  Results are bit-exact.
  * Errors: EINVAL (null pointer, bs < 0, max_budget < 0, depth_max/topk < 1
  * with max_budget > 0, max_budget unreachable); EUNSUPPORTED when
- * depth_max * ceil(log2(topk)) > 64 (rank paths are packed in 64 bits).
+ * depth_max * ceil(log2(topk)) > 64 (rank paths are packed in 64 bits),
+ * max_budget > 2048, or depth_max * topk > 8192 (with max_budget > 0).
  * A request whose budget exceeds max_budget gets only max_budget draft nodes;
  * its remaining node slots are written as token -1, parent -1, depth -1.
  */
@@ -211,7 +213,8 @@ int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t num_slots,
  * and lse + l * lse_layer_stride (strides in elements of each array; a zero
  * input stride shares one array across layers); every other argument and
  * the result of each layer are exactly those of ddtree_verify_attn.  Layer
- * outputs must not overlap.  Small layers share one launch; a layer whose
+ * outputs must not overlap: with num_layers > 1, out_layer_stride (and
+ * lse_layer_stride when lse is given) must be nonzero (EINVAL otherwise).  Small layers share one launch; a layer whose
  * work alone fills the device (bf16, automatic split, at least 64 KV blocks
  * of 32 columns per compute unit by the host bounds) gets a launch of its
  * own, still enqueued by this one call.  Useful where the queries of several layers are
@@ -257,7 +260,8 @@ int ddtree_verify_attn_layers(int num_layers, const void* q, int64_t q_layer_str
  *                  (accept_len tokens), -1 padded.
  *   bonus_tokens   [bs] i32: target argmax at the last accepted node.
  * If two children of one node carry the same token the smaller index wins.
- * Errors: EINVAL (null pointer, bs < 0, depth_max < 0).  A request with
+ * Errors: EINVAL (null pointer, bs < 0, depth_max < 0), EUNSUPPORTED
+ * (depth_max > 4096).  A request with
  * Q_r < 1 gets accept_len 0 and all -1 rows.
  */
 int ddtree_accept(const int32_t* node_tokens, const int32_t* node_parents,
@@ -277,14 +281,16 @@ int ddtree_accept(const int32_t* node_tokens, const int32_t* node_parents,
  * as the target row, mass R; children are tried in node order; child c with
  * token t is accepted iff coins[c] * R < res[t], otherwise R -= res[t] and
  * res[t] = 0; the walk stops when no child is accepted or after
- * depth_max + 1 nodes; the bonus is drawn from the residual at the last
- * node by inverse CDF at bonus_uniforms[r] * R.  fp32 with every sum in one
- * fixed order: rows cut into 256 contiguous blocks of ceil(vocab / 256)
- * tokens, each block summed token by token and the blocks one by one; the
- * inverse CDF picks the first block whose running mass plus its own exceeds
- * the threshold, then the first token of it whose running mass does (its
- * last token with mass if rounding leaves it unreached; the row's last
- * token with mass if no block reaches it).
+ * depth_max + 1 nodes; the bonus is the first token whose running residual
+ * mass (vocabulary order) exceeds bonus_uniforms[r] times the residual's
+ * mass at the last node.  Computed in fp32; decisions agree with exact
+ * arithmetic except within the fp32 rounding of the sums, about
+ * (ceil(vocab / 256) + 256 + nodes) * 2^-24 of the row's mass (each sum
+ * runs over 256 contiguous blocks of ceil(vocab / 256) tokens, the tokens
+ * of a block one by one, then the blocks one by one, so a call's result
+ * does not depend on timing).  A token without mass is never accepted or
+ * drawn; if rounding leaves the threshold unreached, the residual's last
+ * token with mass is drawn.
  *
  *   node_tokens, node_parents [total_q] i32; qo_indptr [bs+1] i32.
  *   target_probs [total_q, vocab] f32: non-negative (temperature, top-k and
@@ -351,6 +357,12 @@ int ddtree_tree_sample(const int32_t* node_tokens, const int32_t* node_parents,
  * is clamped (accept_len to [0, min(Q_r, depth_max+1)], node ids to the
  * request, slots to the pool); the affected outputs are unspecified.
  */
+int ddtree_commit_kv(const int32_t* kv_indptr, const int32_t* kv_indices,
+                     const int32_t* qo_indptr, const int32_t* accepted_nodes,
+                     const int32_t* accept_len, int bs, int depth_max, int max_kv_len,
+                     int32_t* new_kv_indptr, int32_t* new_kv_indices, long long new_kv_capacity,
+                     void* kv_pool, long long num_slots, int dtype, void* stream);
+
 /*
  * ddtree_drafter_topk -- per-depth top-k log-probabilities of the drafter's
  * logits (the input of ddtree_build_tree).
@@ -363,7 +375,10 @@ int ddtree_tree_sample(const int32_t* node_tokens, const int32_t* node_parents,
  * descending order, equal values in ascending token id.
  *
  *   logits   [rows, vocab] of dtype (DDTREE_F32 or DDTREE_BF16), row-major;
- *            rows = bs * depth_max for a batch of drafts.  Finite or -inf.
+ *            rows = bs * depth_max for a batch of drafts.  Finite or -inf,
+ *            with at least one finite logit per row (a row of only -inf
+ *            has no distribution; its outputs are unspecified).  Long -inf
+ *            runs, e.g. a masked vocabulary tail, are fine.
  *   topk_logprobs [rows, topk] f32 out; topk_ids [rows, topk] i32 out
  *            (exactly the layout ddtree_build_tree reads).
  *   workspace of ddtree_drafter_topk_workspace_size(rows, vocab, topk)
@@ -378,11 +393,44 @@ int ddtree_drafter_topk(const void* logits, int dtype, int rows, int vocab, int 
                         float* topk_logprobs, int32_t* topk_ids, void* workspace,
                         size_t workspace_bytes, void* stream);
 
-int ddtree_commit_kv(const int32_t* kv_indptr, const int32_t* kv_indices,
-                     const int32_t* qo_indptr, const int32_t* accepted_nodes,
-                     const int32_t* accept_len, int bs, int depth_max, int max_kv_len,
-                     int32_t* new_kv_indptr, int32_t* new_kv_indices, long long new_kv_capacity,
-                     void* kv_pool, long long num_slots, int dtype, void* stream);
+/*
+ * ddtree_validate_inputs -- debug check of the index arrays of a verify step
+ * (not needed on the hot path: the other calls trust device data).
+ *
+ * Looks for the marshalling mistakes "The 30-Column Mask ..." describes in
+ * sections "The Fix: Building Combined Indices" and "Mistakes and Incorrect
+ * Assumptions" (a KV index list holding only the prefix slots while the
+ * mask expects prefix + tree columns; offsets that do not line up; slot ids
+ * outside the pool) and offsets taken from the wrong length ("The Mask Bug
+ * That Changed Everything ...", section "The Context: A Cascade of
+ * Infrastructure and Algorithm Challenges").
+ *
+ *   qo_indptr [bs+1], kv_indptr [bs+1], kv_indices [num_kv_indices] i32, as
+ *   for ddtree_verify_attn; total_q = the length of the node arrays;
+ *   num_slots = the pool's rows.
+ *   prefix_lens  nullable [bs] i32: when given, every request must have
+ *                exactly P_r + Q_r KV columns.
+ *   node_parents nullable [total_q] i32: when given, each request's node 0
+ *                must have parent -1 and every other node c a parent in
+ *                [0, c).
+ *   report [2 * DDTREE_NUM_CHECKS] i32, device, written by the call: for
+ *   check k, report[2k] = number of violations and report[2k+1] = the
+ *   smallest offending index (-1 if none).  Checks, in order:
+ *     0 QO_INDPTR  request r with qo[r] < 0, qo[r+1] < qo[r] or qo[r+1] > total_q
+ *     1 KV_INDPTR  request r with kv[r] < 0, kv[r+1] < kv[r] or kv[r+1] > num_kv_indices
+ *     2 KV_LEN     request r with N_r < Q_r, or N_r != P_r + Q_r (prefix_lens given)
+ *     3 KV_INDEX   position j of kv_indices with a slot outside [0, num_slots)
+ *     4 PARENT     node index (into the node arrays) with a bad parent
+ * Every read stays inside the sizes given, whatever the arrays hold.  The
+ * report is ready when the stream reaches it (the caller synchronises).
+ * Errors: EINVAL (null report, negative size, null indptr with bs > 0, null
+ * kv_indices with num_kv_indices > 0), EUNSUPPORTED (bs > 65534).
+ */
+#define DDTREE_NUM_CHECKS 5
+int ddtree_validate_inputs(int bs, const int32_t* qo_indptr, int total_q,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           int64_t num_kv_indices, int64_t num_slots, const int32_t* prefix_lens,
+                           const int32_t* node_parents, int32_t* report, void* stream);
 
 #ifdef __cplusplus
 }

@@ -203,6 +203,13 @@ def test_verify_attn_layers_validation(lib):
     assert call(18, -5) == EINVAL
     assert call(1, NULL) == EINVAL
     assert call(16, 7) == EINVAL                       # dtype
+    assert call(18, 0) == EINVAL and "overlap" in _err(lib)   # layers writing one output
+    a = list(args)
+    a[19], a[20] = FAKE, 0                             # lse given with a zero stride
+    assert f(*a) == EINVAL
+    a = list(args)
+    a[0], a[18] = 1, 0                                 # one layer: stride unused
+    assert f(*a) != EINVAL or "overlap" not in _err(lib)
     # workspace: L single-layer workspaces
     one = lib.ddtree_verify_attn_workspace_size(2, 8, 33, 100, 3, F32)
     assert lib.ddtree_verify_attn_layers_workspace_size(5, 2, 8, 33, 100, 3, F32) == 5 * one
@@ -214,3 +221,17 @@ def test_verify_attn_layers_validation(lib):
     a = list(args)
     a[11] = 0                                          # bs == 0: nothing to do
     assert f(*a) == 0
+
+
+def test_validate_inputs_host_checks(lib):
+    f = lib.ddtree_validate_inputs
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert f(1, FAKE, 10, FAKE, FAKE, 10, 10, NULL, NULL, NULL, NULL) == EINVAL     # no report
+    assert "report" in _err(lib)
+    assert f(-1, FAKE, 10, FAKE, FAKE, 10, 10, NULL, NULL, FAKE, NULL) == EINVAL
+    assert f(1, NULL, 10, FAKE, FAKE, 10, 10, NULL, NULL, FAKE, NULL) == EINVAL
+    assert f(1, FAKE, 10, FAKE, NULL, 10, 10, NULL, NULL, FAKE, NULL) == EINVAL
+    assert f(70000, FAKE, 10, FAKE, FAKE, 10, 10, NULL, NULL, FAKE, NULL) == EUNSUPPORTED

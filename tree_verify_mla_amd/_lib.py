@@ -70,6 +70,8 @@ def load() -> ctypes.CDLL:
     lib.ddtree_commit_kv.restype = I
     lib.ddtree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, P, P, ctypes.c_longlong, P,
                                      ctypes.c_longlong, I, P]
+    lib.ddtree_validate_inputs.restype = I
+    lib.ddtree_validate_inputs.argtypes = [I, P, I, P, P, I64, I64, P, P, P, P]
     _lib = lib
     return lib
 
@@ -176,6 +178,9 @@ def ddtree_verify_attn_layers(q, kv_pool, kv_indptr, kv_indices, qo_indptr, vis_
         raise ValueError("kv_pool must be [L, num_slots, 576] or [1, num_slots, 576]")
     if out.shape[0] != L or (lse is not None and lse.shape[0] != L):
         raise ValueError("out and lse need one entry per layer")
+    if L > 1 and (out.stride(0) < out[0].numel() or
+                  (lse is not None and lse.stride(0) < lse[0].numel())):
+        raise ValueError("layer outputs must not overlap")
     bs = qo_indptr.numel() - 1
     kv_ls = kv_pool.stride(0) if kv_pool.shape[0] == L and L > 1 else 0
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -254,15 +259,13 @@ def ddtree_tree_sample_workspace_size(total_q: int) -> int:
 def ddtree_tree_sample(node_tokens, node_parents, qo_indptr, target_probs, coins, bonus_uniforms,
                        depth_max: int, accepted_nodes, accept_len, commit_tokens, bonus_tokens,
                        workspace=None, stream=None):
-    """Stochastic acceptance; target_probs [total_q, vocab] f32.  A workspace
-    of ddtree_tree_sample_workspace_size(total_q) bytes is allocated here when
-    none is passed."""
+    """Stochastic acceptance; target_probs [total_q, vocab] f32.  ``workspace``
+    is caller-owned (ddtree_tree_sample_workspace_size(total_q) bytes), as for
+    every other call: nothing is allocated here, so the call can be captured
+    in a graph."""
     bs = qo_indptr.numel() - 1
     total_q, vocab = target_probs.shape
-    if workspace is None:
-        workspace = torch.empty(ddtree_tree_sample_workspace_size(total_q), dtype=torch.uint8,
-                                device=target_probs.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("ddtree_tree_sample", load().ddtree_tree_sample(
         _p(node_tokens, torch.int32, "node_tokens"), _p(node_parents, torch.int32, "node_parents"),
         _p(qo_indptr, torch.int32, "qo_indptr"), _p(target_probs, torch.float32, "target_probs"),
@@ -271,4 +274,23 @@ def ddtree_tree_sample(node_tokens, node_parents, qo_indptr, target_probs, coins
         _p(accepted_nodes, torch.int32, "accepted_nodes"),
         _p(accept_len, torch.int32, "accept_len"), _p(commit_tokens, torch.int32, "commit_tokens"),
         _p(bonus_tokens, torch.int32, "bonus_tokens"), _p(workspace, None, "workspace"), ws_bytes,
+        _stream(stream)))
+
+
+DDTREE_NUM_CHECKS = 5
+CHECK_NAMES = ("QO_INDPTR", "KV_INDPTR", "KV_LEN", "KV_INDEX", "PARENT")
+
+
+def ddtree_validate_inputs(qo_indptr, total_q: int, kv_indptr, kv_indices, num_slots: int,
+                           report, prefix_lens=None, node_parents=None, stream=None):
+    """Debug check of a step's index arrays; ``report`` is an int32 device
+    tensor of 2 * DDTREE_NUM_CHECKS entries (count, first offending index)."""
+    bs = qo_indptr.numel() - 1
+    if report.numel() < 2 * DDTREE_NUM_CHECKS:
+        raise ValueError("report needs 2 * DDTREE_NUM_CHECKS entries")
+    _check("ddtree_validate_inputs", load().ddtree_validate_inputs(
+        bs, _p(qo_indptr, torch.int32, "qo_indptr"), int(total_q),
+        _p(kv_indptr, torch.int32, "kv_indptr"), _p(kv_indices, torch.int32, "kv_indices"),
+        int(kv_indices.numel()), int(num_slots), _p(prefix_lens, torch.int32, "prefix_lens"),
+        _p(node_parents, torch.int32, "node_parents"), _p(report, torch.int32, "report"),
         _stream(stream)))

@@ -396,6 +396,8 @@ int verify_attn_impl(const char* fn, int L, const void* q, long long q_ls, const
                  DDTREE_EINVAL, "%s: null required pointer", fn);
   DDTREE_REQUIRE(q_ls >= 0 && kv_ls >= 0 && out_ls >= 0 && lse_ls >= 0, DDTREE_EINVAL,
                  "%s: layer strides must be >= 0", fn);
+  DDTREE_REQUIRE(L == 1 || (out_ls > 0 && (!lse || lse_ls > 0)), DDTREE_EINVAL,
+                 "%s: layer outputs must not overlap (zero output stride with %d layers)", fn, L);
   DDTREE_REQUIRE(num_heads >= 1, DDTREE_EINVAL, "%s: num_heads must be >= 1", fn);
   DDTREE_REQUIRE(max_q_len >= 1, DDTREE_EINVAL, "%s: max_q_len must be >= 1", fn);
   DDTREE_REQUIRE(max_kv_len >= max_q_len, DDTREE_EINVAL,
