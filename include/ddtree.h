@@ -318,6 +318,28 @@ int ddtree_tree_sample(const int32_t* node_tokens, const int32_t* node_parents,
                        void* stream);
 
 /*
+ * ddtree_tree_sample_noalloc -- ddtree_tree_sample without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments (less the workspace), same kernels and same results as
+ * ddtree_tree_sample.  Its scratch (the block masses of every row) is a
+ * static device array of the library, 8 MiB, holding up to 4096 tree nodes:
+ * each GPU the call runs on keeps its own copy until the process ends.  The
+ * call allocates nothing (its first call on a device looks the array's
+ * address up once).  Calls that overlap on one GPU share that array and
+ * race: serialise them (one stream, or events).
+ * Errors: those of ddtree_tree_sample (no EWORKSPACE), EUNSUPPORTED for
+ * total_q > 4096, EHIP if the array's address cannot be found.
+ */
+int ddtree_tree_sample_noalloc(const int32_t* node_tokens, const int32_t* node_parents,
+                               const int32_t* qo_indptr, const float* target_probs,
+                               const float* coins, const float* bonus_uniforms, int bs,
+                               int total_q, int depth_max, int vocab, int32_t* accepted_nodes,
+                               int32_t* accept_len, int32_t* commit_tokens,
+                               int32_t* bonus_tokens, void* stream);
+
+/*
  * ddtree_commit_kv -- the accepted path enters each request's KV cache.
  *
  * Defined by "The Architecture of a Speculative Decoding Engine ...",

@@ -70,6 +70,8 @@ def load() -> ctypes.CDLL:
     lib.ddtree_commit_kv.restype = I
     lib.ddtree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, P, P, ctypes.c_longlong, P,
                                      ctypes.c_longlong, I, P]
+    lib.ddtree_tree_sample_noalloc.restype = I
+    lib.ddtree_tree_sample_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, P, P, P]
     lib.ddtree_validate_inputs.restype = I
     lib.ddtree_validate_inputs.argtypes = [I, P, I, P, P, I64, I64, P, P, P, P]
     _lib = lib
@@ -294,3 +296,20 @@ def ddtree_validate_inputs(qo_indptr, total_q: int, kv_indptr, kv_indices, num_s
         int(kv_indices.numel()), int(num_slots), _p(prefix_lens, torch.int32, "prefix_lens"),
         _p(node_parents, torch.int32, "node_parents"), _p(report, torch.int32, "report"),
         _stream(stream)))
+
+
+def ddtree_tree_sample_noalloc(node_tokens, node_parents, qo_indptr, target_probs, coins,
+                               bonus_uniforms, depth_max: int, accepted_nodes, accept_len,
+                               commit_tokens, bonus_tokens, stream=None):
+    """ddtree_tree_sample on the library's built-in scratch (no workspace,
+    at most 4096 tree nodes)."""
+    bs = qo_indptr.numel() - 1
+    total_q, vocab = target_probs.shape
+    _check("ddtree_tree_sample_noalloc", load().ddtree_tree_sample_noalloc(
+        _p(node_tokens, torch.int32, "node_tokens"), _p(node_parents, torch.int32, "node_parents"),
+        _p(qo_indptr, torch.int32, "qo_indptr"), _p(target_probs, torch.float32, "target_probs"),
+        _p(coins, torch.float32, "coins"), _p(bonus_uniforms, torch.float32, "bonus_uniforms"),
+        bs, int(total_q), int(depth_max), int(vocab),
+        _p(accepted_nodes, torch.int32, "accepted_nodes"),
+        _p(accept_len, torch.int32, "accept_len"), _p(commit_tokens, torch.int32, "commit_tokens"),
+        _p(bonus_tokens, torch.int32, "bonus_tokens"), _stream(stream)))

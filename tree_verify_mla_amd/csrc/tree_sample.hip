@@ -31,6 +31,9 @@
 // takes the decisions from those masses and the children's probabilities,
 // and for the bonus re-sums only the blocks that hold rejected tokens and
 // scans the one block the threshold falls in.
+#include <mutex>
+#include <vector>
+
 #include "common.h"
 
 namespace {
@@ -358,6 +361,73 @@ __global__ __launch_bounds__(WT) void walk_kernel(
   }
 }
 
+// The launches of one call, the block masses in bm / bl.
+int launch_sample(const int32_t* node_tokens, const int32_t* node_parents,
+                  const int32_t* qo_indptr, const float* target_probs, const float* coins,
+                  const float* bonus_uniforms, int bs, int total_q, int depth_max, int vocab,
+                  int32_t* accepted_nodes, int32_t* accept_len, int32_t* commit_tokens,
+                  int32_t* bonus_tokens, float* bm, int* bl, hipStream_t s) {
+  const int per = (vocab + NB - 1) / NB;
+  if (total_q > 0) {
+    hipLaunchKernelGGL(block_mass_kernel, dim3(total_q, NB / GB), dim3(256), 0, s, target_probs,
+                       vocab, per, bm, bl);
+    const int rc = ddtree::check_launch("tree_sample");
+    if (rc != DDTREE_OK) return rc;
+  }
+  hipLaunchKernelGGL(walk_kernel, dim3(bs), dim3(WT), 0, s, node_tokens, node_parents, qo_indptr,
+                     target_probs, coins, bonus_uniforms, total_q, depth_max, vocab, per, bm, bl,
+                     accepted_nodes, accept_len, commit_tokens, bonus_tokens);
+  return ddtree::check_launch("tree_sample");
+}
+
+// Host checks shared by both entry points (everything but the workspace).
+int check_args(const char* fn, const int32_t* node_tokens, const int32_t* node_parents,
+               const int32_t* qo_indptr, const float* target_probs, const float* coins,
+               const float* bonus_uniforms, int bs, int total_q, int depth_max, int vocab,
+               int32_t* accepted_nodes, int32_t* accept_len, int32_t* commit_tokens,
+               int32_t* bonus_tokens) {
+  DDTREE_REQUIRE(node_tokens && node_parents && qo_indptr && target_probs && coins &&
+                     bonus_uniforms && accepted_nodes && accept_len && commit_tokens &&
+                     bonus_tokens,
+                 DDTREE_EINVAL, "%s: null required pointer", fn);
+  DDTREE_REQUIRE(total_q >= 0, DDTREE_EINVAL, "%s: total_q must be >= 0", fn);
+  DDTREE_REQUIRE(depth_max >= 0, DDTREE_EINVAL, "%s: depth_max must be >= 0", fn);
+  DDTREE_REQUIRE(vocab >= 1, DDTREE_EINVAL, "%s: vocab must be >= 1", fn);
+  DDTREE_REQUIRE((long long)vocab <= (long long)NB * STAGE, DDTREE_EUNSUPPORTED,
+                 "%s: vocab %d above the supported %d", fn, vocab, NB * STAGE);
+  return DDTREE_OK;
+}
+
+// Scratch of the allocation-free entry point: the block masses (floats) and
+// last-token indices (ints) of up to NOALLOC_MAX_Q rows.  Every call on a
+// device uses that device's copy; the kernels overwrite every entry they
+// read, so nothing needs clearing.
+constexpr int NOALLOC_MAX_Q = 4096;
+constexpr size_t NOALLOC_BYTES = (size_t)NOALLOC_MAX_Q * NB * (sizeof(float) + sizeof(int));
+__device__ __align__(256) char scratch[NOALLOC_BYTES];
+
+// The device address of the current device's scratch, looked up once per
+// device with that device current (host code never uses the array's name as
+// an address).
+int scratch_ptr(char** out) {
+  static std::mutex mu;
+  static std::vector<char*> ptrs;
+  int dev = 0;
+  DDTREE_REQUIRE(hipGetDevice(&dev) == hipSuccess && dev >= 0, DDTREE_EHIP,
+                 "tree_sample_noalloc: no current device");
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    DDTREE_REQUIRE(e == hipSuccess && p, DDTREE_EHIP,
+                   "tree_sample_noalloc: hipGetSymbolAddress failed: %s", hipGetErrorString(e));
+    ptrs[dev] = static_cast<char*>(p);
+  }
+  *out = ptrs[dev];
+  return DDTREE_OK;
+}
+
 }  // namespace
 
 extern "C" size_t ddtree_tree_sample_workspace_size(int total_q) {
@@ -374,31 +444,44 @@ extern "C" int ddtree_tree_sample(const int32_t* node_tokens, const int32_t* nod
   ddtree::clear_error();
   DDTREE_REQUIRE(bs >= 0, DDTREE_EINVAL, "tree_sample: bs must be >= 0");
   if (bs == 0) return DDTREE_OK;
-  DDTREE_REQUIRE(node_tokens && node_parents && qo_indptr && target_probs && coins &&
-                     bonus_uniforms && accepted_nodes && accept_len && commit_tokens &&
-                     bonus_tokens,
-                 DDTREE_EINVAL, "tree_sample: null required pointer");
-  DDTREE_REQUIRE(total_q >= 0, DDTREE_EINVAL, "tree_sample: total_q must be >= 0");
-  DDTREE_REQUIRE(depth_max >= 0, DDTREE_EINVAL, "tree_sample: depth_max must be >= 0");
-  DDTREE_REQUIRE(vocab >= 1, DDTREE_EINVAL, "tree_sample: vocab must be >= 1");
-  DDTREE_REQUIRE((long long)vocab <= (long long)NB * STAGE, DDTREE_EUNSUPPORTED,
-                 "tree_sample: vocab %d above the supported %d", vocab, NB * STAGE);
+  int rc = check_args("tree_sample", node_tokens, node_parents, qo_indptr, target_probs, coins,
+                      bonus_uniforms, bs, total_q, depth_max, vocab, accepted_nodes, accept_len,
+                      commit_tokens, bonus_tokens);
+  if (rc != DDTREE_OK) return rc;
   const size_t need = ddtree_tree_sample_workspace_size(total_q);
   DDTREE_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), DDTREE_EWORKSPACE,
                  "tree_sample: workspace of %zu bytes needed (got %zu)", need,
                  workspace ? workspace_bytes : (size_t)0);
-  const int per = (vocab + NB - 1) / NB;
   float* bm = static_cast<float*>(workspace);
   int* bl = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)total_q * NB * sizeof(float));
-  hipStream_t s = ddtree::as_stream(stream);
-  if (total_q > 0) {
-    hipLaunchKernelGGL(block_mass_kernel, dim3(total_q, NB / GB), dim3(256), 0, s, target_probs,
-                       vocab, per, bm, bl);
-    const int rc = ddtree::check_launch("tree_sample");
-    if (rc != DDTREE_OK) return rc;
-  }
-  hipLaunchKernelGGL(walk_kernel, dim3(bs), dim3(WT), 0, s, node_tokens, node_parents, qo_indptr,
-                     target_probs, coins, bonus_uniforms, total_q, depth_max, vocab, per, bm, bl,
-                     accepted_nodes, accept_len, commit_tokens, bonus_tokens);
-  return ddtree::check_launch("tree_sample");
+  return launch_sample(node_tokens, node_parents, qo_indptr, target_probs, coins, bonus_uniforms,
+                       bs, total_q, depth_max, vocab, accepted_nodes, accept_len, commit_tokens,
+                       bonus_tokens, bm, bl, ddtree::as_stream(stream));
+}
+
+extern "C" int ddtree_tree_sample_noalloc(const int32_t* node_tokens, const int32_t* node_parents,
+                                          const int32_t* qo_indptr, const float* target_probs,
+                                          const float* coins, const float* bonus_uniforms, int bs,
+                                          int total_q, int depth_max, int vocab,
+                                          int32_t* accepted_nodes, int32_t* accept_len,
+                                          int32_t* commit_tokens, int32_t* bonus_tokens,
+                                          void* stream) {
+  ddtree::clear_error();
+  DDTREE_REQUIRE(bs >= 0, DDTREE_EINVAL, "tree_sample_noalloc: bs must be >= 0");
+  if (bs == 0) return DDTREE_OK;
+  int rc = check_args("tree_sample_noalloc", node_tokens, node_parents, qo_indptr, target_probs,
+                      coins, bonus_uniforms, bs, total_q, depth_max, vocab, accepted_nodes,
+                      accept_len, commit_tokens, bonus_tokens);
+  if (rc != DDTREE_OK) return rc;
+  DDTREE_REQUIRE(total_q <= NOALLOC_MAX_Q, DDTREE_EUNSUPPORTED,
+                 "tree_sample_noalloc: total_q %d above the built-in scratch's %d rows", total_q,
+                 NOALLOC_MAX_Q);
+  char* base = nullptr;
+  rc = scratch_ptr(&base);
+  if (rc != DDTREE_OK) return rc;
+  float* bm = reinterpret_cast<float*>(base);
+  int* bl = reinterpret_cast<int*>(base + (size_t)NOALLOC_MAX_Q * NB * sizeof(float));
+  return launch_sample(node_tokens, node_parents, qo_indptr, target_probs, coins, bonus_uniforms,
+                       bs, total_q, depth_max, vocab, accepted_nodes, accept_len, commit_tokens,
+                       bonus_tokens, bm, bl, ddtree::as_stream(stream));
 }
