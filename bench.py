@@ -399,8 +399,7 @@ def main():
         st = steps[i % R]
         e = ev[i]
         e[0].record(stream)
-        st.build(stream)
-        st.visibility(stream)
+        st.build_visibility(stream)
         e[1].record(stream)
         st.attention(stream)
         e[2].record(stream)

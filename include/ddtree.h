@@ -6,6 +6,7 @@
  *   ddtree_drafter_topk        per-depth top-k log-probs of the drafter's logits
  *   ddtree_build_tree          best-first draft tree from per-depth top-k log-probs
  *   ddtree_compile_visibility  ancestor-or-self bitsets (+ positions, + dense mask)
+ *   ddtree_build_tree_visibility  (or) the two above in one call
  *   ddtree_verify_attn         absorbed-MLA attention of every tree node x head
  *                              over the shared prefix plus its own ancestors
  *   ddtree_verify_attn_layers  (or) the same over several layers in one launch
@@ -138,6 +139,29 @@ int ddtree_compile_visibility(const int32_t* node_parents, const int32_t* node_d
                               int max_q_len, int words_per_row, uint32_t* vis_bits,
                               int64_t* positions, uint8_t* dense_mask,
                               const int64_t* mask_indptr, void* stream);
+
+/*
+ * ddtree_build_tree_visibility -- ddtree_build_tree followed by
+ * ddtree_compile_visibility (bitsets and positions, no dense mask) in one
+ * call: the same outputs, bit for bit, as the two calls in sequence.
+ *
+ * Both operations are defined where the two calls are.  For budgets up to
+ * 64 with depth_max * topk <= 256 and max_q_len <= 128 it is one launch:
+ * each node's ancestor-or-self bitset is its parent's bits plus its own,
+ * formed as the node is taken (a parent is always taken before its child);
+ * other sizes run the two calls' kernels back to back.
+ *   Arguments: those of ddtree_build_tree, then prefix_lens, max_q_len,
+ *   words_per_row, vis_bits and positions as for ddtree_compile_visibility
+ *   (node_depths is always written; positions nullable, needs prefix_lens).
+ * Errors: those of both calls.
+ */
+int ddtree_build_tree_visibility(const float* topk_logprobs, const int32_t* topk_ids,
+                                 const int32_t* root_tokens, const int32_t* qo_indptr,
+                                 const int32_t* prefix_lens, int bs, int depth_max, int topk,
+                                 int max_budget, int max_q_len, int words_per_row,
+                                 int32_t* node_tokens, int32_t* node_parents,
+                                 int32_t* node_depths, float* node_scores, uint32_t* vis_bits,
+                                 int64_t* positions, void* stream);
 
 /*
  * ddtree_verify_attn_workspace_size -- bytes of device workspace that

@@ -235,3 +235,26 @@ def test_validate_inputs_host_checks(lib):
     assert f(1, NULL, 10, FAKE, FAKE, 10, 10, NULL, NULL, FAKE, NULL) == EINVAL
     assert f(1, FAKE, 10, FAKE, NULL, 10, 10, NULL, NULL, FAKE, NULL) == EINVAL
     assert f(70000, FAKE, 10, FAKE, FAKE, 10, 10, NULL, NULL, FAKE, NULL) == EUNSUPPORTED
+
+
+def test_build_tree_visibility_validation(lib):
+    f = lib.ddtree_build_tree_visibility
+    # lp, ids, roots, qo, prefix, bs, D, K, max_budget, max_q, W, tok, par, dep, sc, bits, pos, stream
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 7, 8, 32, 33, 2, FAKE, FAKE, FAKE, NULL, FAKE, NULL, NULL]
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(5, -1) == EINVAL
+    assert call(2, NULL) == EINVAL                  # root tokens
+    a = list(args)
+    a[6], a[7], a[8] = 2, 2, 7                      # 2 + 4 rank paths cannot hold 7 nodes
+    assert f(*a) == EINVAL and "reachable" in _err(lib)
+    assert call(8, 4096) == EUNSUPPORTED            # above 2048
+    assert call(10, 1) == EINVAL and "words_per_row" in _err(lib)
+    assert call(15, NULL) == EINVAL                 # vis_bits
+    a = list(args)
+    a[16], a[4] = FAKE, NULL                        # positions without prefix_lens
+    assert f(*a) == EINVAL
+    assert call(9, 0) == EINVAL                     # max_q_len
+    assert call(5, 0) == 0                          # empty batch

@@ -190,11 +190,14 @@ def test_dense_mask_matches_oracle():
 def test_build_tree_exact_many_shapes():
     """Bit-exact trees over depth/top-k/budget combinations, incl. ties."""
     _say("test_build_tree_exact_many_shapes")
-    # budgets above 126 take the LDS-frontier kernel, the others the register
-    # one; depth x top-k above 256 keeps the top-k table in LDS
+    # budgets up to 64 (depth x top-k up to 256) take the lean register
+    # builder, which also forms the bitsets in the one-call form; budgets up
+    # to 126 the two-slot register builder; above that the LDS-frontier one;
+    # depth x top-k above 256 keeps the top-k table in LDS
     for (D, K, budgets) in [(7, 4, [8, 0, 3]), (7, 8, [32, 16, 64]), (7, 16, [64, 1, 40]),
                             (3, 2, [14, 7, 1]), (1, 5, [5, 2, 0]), (7, 8, [126, 125, 2]),
-                            (7, 8, [200, 127, 9]), (7, 40, [100, 12, 3])]:
+                            (7, 8, [200, 127, 9]), (7, 40, [100, 12, 3]), (8, 32, [64, 63, 5]),
+                            (2, 64, [64, 33, 1]), (6, 1, [6, 3, 0])]:
         wl = make_workload(get_config(3), bs=3, heads=1, depth=D, topk=K, budgets=budgets,
                            prefixes=[4, 4, 4], pool_slots=400, seed=77 + D * K)
         # coarse log-probs give exact fp32 ties in the scores
@@ -208,6 +211,20 @@ def test_build_tree_exact_many_shapes():
         assert np.array_equal(st.node_tokens.cpu().numpy(), orc.tokens), (D, K)
         assert np.array_equal(st.node_parents.cpu().numpy(), orc.parents), (D, K)
         assert np.array_equal(st.node_depths.cpu().numpy(), orc.depths), (D, K)
+        sc = st.node_scores.cpu().numpy().view(np.uint32)
+        assert np.array_equal(sc, orc.scores.view(np.uint32)), (D, K)
+        # the same tree, bitsets and positions from the one-call form
+        st2 = VerifyStep(x)
+        for t in (st2.node_tokens, st2.node_parents, st2.node_depths, st2.vis_bits, st2.positions):
+            t.fill_(-7)
+        st2.build_visibility()
+        torch.cuda.synchronize()
+        for a, b in ((st2.node_tokens, orc.tokens), (st2.node_parents, orc.parents),
+                     (st2.node_depths, orc.depths)):
+            assert np.array_equal(a.cpu().numpy(), b), (D, K, "one-call form")
+        assert np.array_equal(st2.node_scores.cpu().numpy().view(np.uint32), sc), (D, K)
+        assert np.array_equal(st2.vis_bits.cpu().numpy().view(np.uint32), orc.bits), (D, K)
+        assert np.array_equal(st2.positions.cpu().numpy(), orc.positions), (D, K)
 
 
 def test_accept_sentinel_and_full_chain():

@@ -46,6 +46,9 @@ def load() -> ctypes.CDLL:
     lib.ddtree_last_error.argtypes = []
     lib.ddtree_build_tree.restype = I
     lib.ddtree_build_tree.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P]
+    lib.ddtree_build_tree_visibility.restype = I
+    lib.ddtree_build_tree_visibility.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P,
+                                                 P]
     lib.ddtree_compile_visibility.restype = I
     lib.ddtree_compile_visibility.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P]
     lib.ddtree_verify_attn_workspace_size.restype = SZ
@@ -115,6 +118,21 @@ def ddtree_build_tree(topk_logprobs, topk_ids, root_tokens, qo_indptr, max_budge
         bs, D, K, int(max_budget), _p(node_tokens, torch.int32, "node_tokens"),
         _p(node_parents, torch.int32, "node_parents"), _p(node_depths, torch.int32, "node_depths"),
         _p(node_scores, torch.float32, "node_scores"), _stream(stream)))
+
+
+def ddtree_build_tree_visibility(topk_logprobs, topk_ids, root_tokens, qo_indptr, prefix_lens,
+                                 max_budget: int, max_q_len: int, node_tokens, node_parents,
+                                 node_depths, vis_bits, node_scores=None, positions=None,
+                                 stream=None):
+    bs, D, K = topk_logprobs.shape
+    _check("ddtree_build_tree_visibility", load().ddtree_build_tree_visibility(
+        _p(topk_logprobs, torch.float32, "topk_logprobs"), _p(topk_ids, torch.int32, "topk_ids"),
+        _p(root_tokens, torch.int32, "root_tokens"), _p(qo_indptr, torch.int32, "qo_indptr"),
+        _p(prefix_lens, torch.int32, "prefix_lens"), bs, D, K, int(max_budget), int(max_q_len),
+        vis_bits.shape[1], _p(node_tokens, torch.int32, "node_tokens"),
+        _p(node_parents, torch.int32, "node_parents"), _p(node_depths, torch.int32, "node_depths"),
+        _p(node_scores, torch.float32, "node_scores"), _p(vis_bits, torch.int32, "vis_bits"),
+        _p(positions, torch.int64, "positions"), _stream(stream)))
 
 
 def ddtree_compile_visibility(node_parents, node_depths, qo_indptr, prefix_lens, max_q_len: int,

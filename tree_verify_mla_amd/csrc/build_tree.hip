@@ -399,6 +399,272 @@ __global__ __launch_bounds__(64) void build_tree_reg_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Lean builder (budget <= LEAN_MAX_BUDGET, depth_max * topk <= 64 * TAB)
+// ---------------------------------------------------------------------------
+// At pop k the frontier holds at most k entries, so budgets up to 64 need
+// one entry per lane.  A pop reads the taken entry with readlane and
+// rewrites only the lanes that change (its slot, and the appended sibling):
+// one select per field, where two frontier entries per lane cost twice the
+// selects and twice the reduction inputs.  The node records (token,
+// parent, depth, score) stay in registers too -- node i in lane i & 63,
+// slot i >> 6 -- and go to memory once at the end, as does the optional
+// visibility: node k's ancestor-or-self bitset is its parent's plus bit k,
+// formed when k is taken (parents are taken before their children), so the
+// bitsets and positions of ddtree_compile_visibility come out of the same
+// launch.
+constexpr int LEAN_MAX_BUDGET = 64;
+constexpr int LEAN_SLOTS = 2;   // node records per lane: up to 128 nodes in registers
+constexpr int LEAN_WORDS = 4;   // bitset words per node record (128 nodes)
+
+// reg with lane lane_idx (uniform) set to v (uniform): one compare, shared by
+// the fields written to one lane, and one select each
+__device__ inline uint32_t wl(uint32_t reg, int lane_idx, uint32_t v) {
+  return (int)threadIdx.x == lane_idx ? v : reg;
+}
+
+template <int TAB, bool VIS>
+__global__ __launch_bounds__(64) void build_lean_kernel(
+    const float* __restrict__ lp, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ roots, const int32_t* __restrict__ qo, int D, int K,
+    int max_budget, int rank_bits, int32_t* __restrict__ tok, int32_t* __restrict__ par,
+    int32_t* __restrict__ dep, float* __restrict__ sc, const int32_t* __restrict__ prefix, int W,
+    uint32_t* __restrict__ bits, int64_t* __restrict__ positions) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int base = qo[r];
+  const int Q = qo[r + 1] - base;
+  if (Q < 1) return;
+  const int B = min(Q - 1, max_budget);
+  const int DK = D * K;
+  // the request's tables: entry i in lane i & 63, register i >> 6
+  uint32_t tl[TAB], ti[TAB];
+#pragma unroll
+  for (int j = 0; j < TAB; ++j) {
+    const int i = lane + 64 * j;
+    const bool in = B > 0 && i < DK;
+    tl[j] = in ? __float_as_uint(lp[(size_t)r * DK + i]) : 0u;
+    ti[j] = in ? (uint32_t)ids[(size_t)r * DK + i] : 0u;
+  }
+  const int32_t root_tok = roots[r];
+  auto tab = [&](const uint32_t* t, int i) {  // entry i (uniform)
+    uint32_t v = t[0];
+#pragma unroll
+    for (int j = 1; j < TAB; ++j) v = (i >> 6) == j ? t[j] : v;
+    return lane_val(v, i & 63);
+  };
+
+  // node records: every node starts as "not in the tree" (token, parent and
+  // depth -1, score 0, only its own bit), the root as itself
+  int32_t n_tok[LEAN_SLOTS], n_par[LEAN_SLOTS], n_dep[LEAN_SLOTS];
+  uint32_t n_sc[LEAN_SLOTS], n_vis[LEAN_SLOTS][LEAN_WORDS];
+#pragma unroll
+  for (int q = 0; q < LEAN_SLOTS; ++q) {
+    const int i = lane + 64 * q;
+    const bool root = i == 0;
+    n_tok[q] = root ? root_tok : -1;
+    n_par[q] = -1;
+    n_dep[q] = root ? 0 : -1;
+    n_sc[q] = 0u;
+#pragma unroll
+    for (int w = 0; w < LEAN_WORDS; ++w) n_vis[q][w] = (i >> 5) == w ? 1u << (i & 31) : 0u;
+  }
+
+  // the frontier: one entry per lane (meta 0 = empty)
+  uint32_t fs = 0u, fp = 0u, fm = 0u, flo = 0u, fhi = 0u;
+  if (B > 0 && lane == 0) {  // the root's best child
+    fs = __float_as_uint(__fadd_rn(0.f, __uint_as_float(tl[0])));
+    fm = pack_meta(1, 0, 0);
+  }
+  int n = 1;
+  for (int k = 1; k <= B; ++k) {
+    // 1. the best entry: largest score key, ties resolved exactly
+    const uint32_t key = fm ? score_key(__uint_as_float(fs)) : 0u;
+    const uint32_t kmax = wave_ext<true>(key);
+    if (kmax == 0u) break;  // empty frontier: only reachable if preconditions are broken
+    uint64_t hit = __ballot(key == kmax);
+    if (__popcll(hit) > 1) {  // rare: equal scores
+      bool tt = (hit >> lane) & 1;
+      const uint32_t dmin = wave_ext<false>(tt ? (fm & 0x7f) : ~0u);
+      tt = tt && (fm & 0x7f) == dmin;
+      const uint32_t hmin = wave_ext<false>(tt ? fhi : ~0u);
+      tt = tt && fhi == hmin;
+      const uint32_t lmin = wave_ext<false>(tt ? flo : ~0u);
+      tt = tt && flo == lmin;
+      hit = __ballot(tt);
+    }
+    const int e = __ffsll((unsigned long long)hit) - 1;
+    const float w_score = __uint_as_float(lane_val(fs, e));
+    const float w_ps = __uint_as_float(lane_val(fp, e));
+    const uint32_t w_meta = lane_val(fm, e);
+    const uint64_t code = ((uint64_t)lane_val(fhi, e) << 32) | lane_val(flo, e);
+    const int d = meta_depth(w_meta), rk = meta_rank(w_meta), p = meta_parent(w_meta);
+
+    // 2. node k (its record in lane k & 63, slot k >> 6)
+    const int32_t t_id = (int32_t)tab(ti, (d - 1) * K + rk);
+    const int kl = k & 63, ks = k >> 6;
+#pragma unroll
+    for (int q = 0; q < LEAN_SLOTS; ++q) {
+      if (q != ks) continue;
+      n_tok[q] = (int32_t)wl((uint32_t)n_tok[q], kl, (uint32_t)t_id);
+      n_par[q] = (int32_t)wl((uint32_t)n_par[q], kl, (uint32_t)p);
+      n_dep[q] = (int32_t)wl((uint32_t)n_dep[q], kl, (uint32_t)d);
+      n_sc[q] = wl(n_sc[q], kl, __float_as_uint(w_score));
+    }
+    if constexpr (VIS) {  // bits of node k = bits of its parent, plus bit k
+#pragma unroll
+      for (int w = 0; w < LEAN_WORDS; ++w) {
+        const uint32_t pv = (p >> 6) == 0 ? lane_val(n_vis[0][w], p & 63)
+                                          : lane_val(n_vis[LEAN_SLOTS - 1][w], p & 63);
+        const uint32_t nv = pv | ((k >> 5) == w ? 1u << (k & 31) : 0u);
+#pragma unroll
+        for (int q = 0; q < LEAN_SLOTS; ++q)
+          if (q == ks) n_vis[q][w] = wl(n_vis[q][w], kl, nv);
+      }
+    }
+    if (k == B) break;  // no further pop reads the frontier
+
+    // 3. successors: the best child takes slot e, the sibling slot n (or e)
+    const bool has_child = d < D, has_sib = rk + 1 < K;
+    const float lp_child = __uint_as_float(tab(tl, min(d, D - 1) * K));
+    const float lp_sib = __uint_as_float(tab(tl, (d - 1) * K + min(rk + 1, K - 1)));
+    const uint64_t cc = code << rank_bits, cs = code + 1;
+    const uint32_t c_s = __float_as_uint(__fadd_rn(w_score, lp_child));
+    const uint32_t s_s = __float_as_uint(__fadd_rn(w_ps, lp_sib));
+    const uint32_t c_m = pack_meta(d + 1, 0, k), s_m = pack_meta(d, rk + 1, p);
+    if (has_child) {
+      fs = wl(fs, e, c_s);
+      fp = wl(fp, e, __float_as_uint(w_score));
+      fm = wl(fm, e, c_m);
+      flo = wl(flo, e, (uint32_t)cc);
+      fhi = wl(fhi, e, (uint32_t)(cc >> 32));
+    }
+    if (has_sib) {
+      const int at = has_child ? n : e;  // n <= k < B <= 64
+      fs = wl(fs, at, s_s);
+      fp = wl(fp, at, __float_as_uint(w_ps));
+      fm = wl(fm, at, s_m);
+      flo = wl(flo, at, (uint32_t)cs);
+      fhi = wl(fhi, at, (uint32_t)(cs >> 32));
+      n += has_child ? 1 : 0;
+    }
+    if (!has_child && !has_sib) fm = wl(fm, e, 0u);
+  }
+
+  // 4. the records (and bitsets, positions) to memory, one store per lane
+  const int64_t P = VIS && positions ? (int64_t)max(prefix[r], 0) : 0;
+#pragma unroll
+  for (int q = 0; q < LEAN_SLOTS; ++q) {
+    const int i = lane + 64 * q;
+    if (i >= Q) break;
+    tok[base + i] = n_tok[q];
+    par[base + i] = n_par[q];
+    dep[base + i] = n_dep[q];
+    if (sc) sc[base + i] = __uint_as_float(n_sc[q]);
+    if constexpr (VIS) {
+      for (int w = 0; w < W; ++w) bits[(size_t)(base + i) * W + w] = w < LEAN_WORDS ? n_vis[q][w] : 0u;
+      if (positions) positions[base + i] = P + n_dep[q];
+    }
+  }
+  // nodes past the records (only when the device data exceeds the host bounds)
+  for (int i = 64 * LEAN_SLOTS + lane; i < Q; i += 64) {
+    tok[base + i] = -1;
+    par[base + i] = -1;
+    dep[base + i] = -1;
+    if (sc) sc[base + i] = 0.f;
+    if constexpr (VIS) {
+      for (int w = 0; w < W; ++w) bits[(size_t)(base + i) * W + w] = (i >> 5) == w ? 1u << (i & 31) : 0u;
+      if (positions) positions[base + i] = P - 1;
+    }
+  }
+}
+}  // namespace
+
+namespace {
+
+// Host checks of ddtree_build_tree's arguments; fills rank_bits.
+int check_build(const char* fn, const float* topk_logprobs, const int32_t* topk_ids,
+                const int32_t* root_tokens, const int32_t* qo_indptr, int bs, int depth_max,
+                int topk, int max_budget, int32_t* node_tokens, int32_t* node_parents,
+                int32_t* node_depths, int& rank_bits) {
+  DDTREE_REQUIRE(root_tokens && qo_indptr && node_tokens && node_parents && node_depths,
+                 DDTREE_EINVAL, "%s: null required pointer", fn);
+  if (max_budget > 0) {
+    DDTREE_REQUIRE(topk_logprobs && topk_ids, DDTREE_EINVAL, "%s: null top-k input", fn);
+    DDTREE_REQUIRE(depth_max >= 1 && topk >= 1, DDTREE_EINVAL,
+                   "%s: depth_max and topk must be >= 1 for a non-empty tree", fn);
+    // reachable = sum_{d=1..D} K^d, saturating
+    long long reach = 0, pw = 1;
+    for (int d = 1; d <= depth_max && reach < (long long)max_budget; ++d) {
+      pw = (pw > (1LL << 40) / topk) ? (1LL << 40) : pw * topk;
+      reach += pw;
+    }
+    DDTREE_REQUIRE((long long)max_budget <= reach, DDTREE_EINVAL,
+                   "%s: max_budget %d exceeds the %lld reachable rank paths", fn, max_budget,
+                   reach);
+  }
+  rank_bits = 1;
+  while ((1 << rank_bits) < topk) ++rank_bits;
+  DDTREE_REQUIRE(max_budget == 0 || (long long)depth_max * rank_bits <= 64, DDTREE_EUNSUPPORTED,
+                 "%s: depth_max * ceil(log2(topk)) = %lld exceeds 64 bits", fn,
+                 (long long)depth_max * rank_bits);
+  DDTREE_REQUIRE(max_budget <= 2048, DDTREE_EUNSUPPORTED,
+                 "%s: max_budget %d above the supported 2048", fn, max_budget);
+  DDTREE_REQUIRE(max_budget == 0 || (long long)depth_max * topk <= 8192, DDTREE_EUNSUPPORTED,
+                 "%s: depth_max * topk = %lld above the supported 8192", fn,
+                 (long long)depth_max * topk);
+  return DDTREE_OK;
+}
+
+// registers per lane the lean builder needs for the top-k tables (0: not lean)
+int lean_tab(int depth_max, int topk, int max_budget) {
+  if (max_budget > LEAN_MAX_BUDGET || depth_max > 127) return 0;
+  const long long dk = max_budget > 0 ? (long long)depth_max * topk : 1;
+  return dk <= 64 ? 1 : (dk <= 128 ? 2 : (dk <= 256 ? 4 : 0));
+}
+
+template <bool VIS>
+void launch_lean(int tab, int bs, hipStream_t s, const float* lp, const int32_t* ids,
+                 const int32_t* roots, const int32_t* qo, int D, int K, int max_budget,
+                 int rank_bits, int32_t* tok, int32_t* par, int32_t* dep, float* sc,
+                 const int32_t* prefix, int W, uint32_t* bits, int64_t* positions) {
+  auto k = tab == 1 ? build_lean_kernel<1, VIS> : (tab == 2 ? build_lean_kernel<2, VIS> : build_lean_kernel<4, VIS>);
+  hipLaunchKernelGGL(k, dim3(bs), dim3(64), 0, s, lp, ids, roots, qo, D, K, max_budget, rank_bits,
+                     tok, par, dep, sc, prefix, W, bits, positions);
+}
+
+// The tree-building launch of ddtree_build_tree (arguments already checked).
+int launch_build(const float* topk_logprobs, const int32_t* topk_ids, const int32_t* root_tokens,
+                 const int32_t* qo_indptr, int bs, int depth_max, int topk, int max_budget,
+                 int rank_bits, int32_t* node_tokens, int32_t* node_parents, int32_t* node_depths,
+                 float* node_scores, hipStream_t s) {
+  const int tab = lean_tab(depth_max, topk, max_budget);
+  if (tab) {
+    launch_lean<false>(tab, bs, s, topk_logprobs, topk_ids, root_tokens, qo_indptr, depth_max,
+                       topk, max_budget, rank_bits, node_tokens, node_parents, node_depths,
+                       node_scores, nullptr, 0, nullptr, nullptr);
+    return ddtree::check_launch("build_tree");
+  }
+  const size_t staged = max_budget > 0 ? (size_t)depth_max * topk * 8 : 0;  // log-probs + ids
+  if (max_budget <= REG_MAX_BUDGET) {
+    if ((long long)depth_max * topk <= TAB_REGS * 64)
+      hipLaunchKernelGGL(build_tree_reg_kernel<true>, dim3(bs), dim3(64), staged, s, topk_logprobs,
+                         topk_ids, root_tokens, qo_indptr, depth_max, topk, max_budget, rank_bits,
+                         node_tokens, node_parents, node_depths, node_scores);
+    else
+      hipLaunchKernelGGL(build_tree_reg_kernel<false>, dim3(bs), dim3(64), staged, s, topk_logprobs,
+                         topk_ids, root_tokens, qo_indptr, depth_max, topk, max_budget, rank_bits,
+                         node_tokens, node_parents, node_depths, node_scores);
+  } else {
+    const size_t lds = (size_t)(max_budget + 2) * (8 + 4 * 5) + staged;
+    hipLaunchKernelGGL(build_tree_kernel, dim3(bs), dim3(64), lds, s, topk_logprobs, topk_ids,
+                       root_tokens, qo_indptr, depth_max, topk, max_budget, rank_bits, node_tokens,
+                       node_parents, node_depths, node_scores);
+  }
+  return ddtree::check_launch("build_tree");
+}
+
 }  // namespace
 
 extern "C" int ddtree_build_tree(const float* topk_logprobs, const int32_t* topk_ids,
@@ -410,50 +676,53 @@ extern "C" int ddtree_build_tree(const float* topk_logprobs, const int32_t* topk
   DDTREE_REQUIRE(bs >= 0, DDTREE_EINVAL, "build_tree: bs must be >= 0 (got %d)", bs);
   DDTREE_REQUIRE(max_budget >= 0, DDTREE_EINVAL, "build_tree: max_budget must be >= 0");
   if (bs == 0) return DDTREE_OK;
-  DDTREE_REQUIRE(root_tokens && qo_indptr && node_tokens && node_parents && node_depths,
-                 DDTREE_EINVAL, "build_tree: null required pointer");
-  if (max_budget > 0) {
-    DDTREE_REQUIRE(topk_logprobs && topk_ids, DDTREE_EINVAL, "build_tree: null top-k input");
-    DDTREE_REQUIRE(depth_max >= 1 && topk >= 1, DDTREE_EINVAL,
-                   "build_tree: depth_max and topk must be >= 1 for a non-empty tree");
-    // reachable = sum_{d=1..D} K^d, saturating
-    long long reach = 0, pw = 1;
-    for (int d = 1; d <= depth_max && reach < (long long)max_budget; ++d) {
-      pw = (pw > (1LL << 40) / topk) ? (1LL << 40) : pw * topk;
-      reach += pw;
-    }
-    DDTREE_REQUIRE((long long)max_budget <= reach, DDTREE_EINVAL,
-                   "build_tree: max_budget %d exceeds the %lld reachable rank paths", max_budget,
-                   reach);
-  }
   int rank_bits = 1;
-  while ((1 << rank_bits) < topk) ++rank_bits;
-  DDTREE_REQUIRE(max_budget == 0 || (long long)depth_max * rank_bits <= 64, DDTREE_EUNSUPPORTED,
-                 "build_tree: depth_max * ceil(log2(topk)) = %lld exceeds 64 bits",
-                 (long long)depth_max * rank_bits);
-  DDTREE_REQUIRE(max_budget <= 2048, DDTREE_EUNSUPPORTED,
-                 "build_tree: max_budget %d above the supported 2048", max_budget);
-  DDTREE_REQUIRE(max_budget == 0 || (long long)depth_max * topk <= 8192, DDTREE_EUNSUPPORTED,
-                 "build_tree: depth_max * topk = %lld above the supported 8192",
-                 (long long)depth_max * topk);
-  const size_t staged = max_budget > 0 ? (size_t)depth_max * topk * 8 : 0;  // log-probs + ids
-  if (max_budget <= REG_MAX_BUDGET) {
-    if ((long long)depth_max * topk <= TAB_REGS * 64)
-      hipLaunchKernelGGL(build_tree_reg_kernel<true>, dim3(bs), dim3(64), staged,
-                         ddtree::as_stream(stream), topk_logprobs, topk_ids, root_tokens, qo_indptr,
-                         depth_max, topk, max_budget, rank_bits, node_tokens, node_parents,
-                         node_depths, node_scores);
-    else
-      hipLaunchKernelGGL(build_tree_reg_kernel<false>, dim3(bs), dim3(64), staged,
-                         ddtree::as_stream(stream), topk_logprobs, topk_ids, root_tokens, qo_indptr,
-                         depth_max, topk, max_budget, rank_bits, node_tokens, node_parents,
-                         node_depths, node_scores);
-  } else {
-    const size_t lds = (size_t)(max_budget + 2) * (8 + 4 * 5) + staged;
-    hipLaunchKernelGGL(build_tree_kernel, dim3(bs), dim3(64), lds, ddtree::as_stream(stream),
-                       topk_logprobs, topk_ids, root_tokens, qo_indptr, depth_max, topk,
-                       max_budget, rank_bits, node_tokens, node_parents, node_depths,
-                       node_scores);
+  int rc = check_build("build_tree", topk_logprobs, topk_ids, root_tokens, qo_indptr, bs, depth_max,
+                       topk, max_budget, node_tokens, node_parents, node_depths, rank_bits);
+  if (rc != DDTREE_OK) return rc;
+  return launch_build(topk_logprobs, topk_ids, root_tokens, qo_indptr, bs, depth_max, topk,
+                      max_budget, rank_bits, node_tokens, node_parents, node_depths, node_scores,
+                      ddtree::as_stream(stream));
+}
+
+// defined in visibility.hip
+int ddtree_visibility_launch(const int32_t* node_parents, const int32_t* node_depths,
+                             const int32_t* qo_indptr, const int32_t* prefix_lens, int bs,
+                             int max_q_len, int words_per_row, uint32_t* vis_bits,
+                             int64_t* positions, hipStream_t s);
+
+extern "C" int ddtree_build_tree_visibility(
+    const float* topk_logprobs, const int32_t* topk_ids, const int32_t* root_tokens,
+    const int32_t* qo_indptr, const int32_t* prefix_lens, int bs, int depth_max, int topk,
+    int max_budget, int max_q_len, int words_per_row, int32_t* node_tokens,
+    int32_t* node_parents, int32_t* node_depths, float* node_scores, uint32_t* vis_bits,
+    int64_t* positions, void* stream) {
+  ddtree::clear_error();
+  const char* fn = "build_tree_visibility";
+  DDTREE_REQUIRE(bs >= 0, DDTREE_EINVAL, "%s: bs must be >= 0 (got %d)", fn, bs);
+  DDTREE_REQUIRE(max_budget >= 0, DDTREE_EINVAL, "%s: max_budget must be >= 0", fn);
+  if (bs == 0) return DDTREE_OK;
+  int rank_bits = 1;
+  int rc = check_build(fn, topk_logprobs, topk_ids, root_tokens, qo_indptr, bs, depth_max, topk,
+                       max_budget, node_tokens, node_parents, node_depths, rank_bits);
+  if (rc != DDTREE_OK) return rc;
+  DDTREE_REQUIRE(max_q_len >= 1, DDTREE_EINVAL, "%s: max_q_len must be >= 1", fn);
+  DDTREE_REQUIRE(vis_bits, DDTREE_EINVAL, "%s: null vis_bits", fn);
+  DDTREE_REQUIRE(!positions || prefix_lens, DDTREE_EINVAL, "%s: positions need prefix_lens", fn);
+  DDTREE_REQUIRE((long long)words_per_row * 32 >= max_q_len, DDTREE_EINVAL,
+                 "%s: words_per_row %d < ceil(max_q_len/32) for max_q_len %d", fn, words_per_row,
+                 max_q_len);
+  hipStream_t s = ddtree::as_stream(stream);
+  const int tab = lean_tab(depth_max, topk, max_budget);
+  if (tab && max_q_len <= 64 * LEAN_SLOTS) {
+    launch_lean<true>(tab, bs, s, topk_logprobs, topk_ids, root_tokens, qo_indptr, depth_max, topk,
+                      max_budget, rank_bits, node_tokens, node_parents, node_depths, node_scores,
+                      prefix_lens, words_per_row, vis_bits, positions);
+    return ddtree::check_launch(fn);
   }
-  return ddtree::check_launch("build_tree");
+  rc = launch_build(topk_logprobs, topk_ids, root_tokens, qo_indptr, bs, depth_max, topk,
+                    max_budget, rank_bits, node_tokens, node_parents, node_depths, node_scores, s);
+  if (rc != DDTREE_OK) return rc;
+  return ddtree_visibility_launch(node_parents, node_depths, qo_indptr, prefix_lens, bs, max_q_len,
+                                  words_per_row, vis_bits, positions, s);
 }

@@ -269,6 +269,7 @@ __global__ __launch_bounds__(128) void merge_lanes_kernel(Params p_all, int G) {
   if (t >= g.T) return;
   MergePlan m;
   if (!merge_plan_fast(p, r, t, g, mt, G, m)) return;
+  if (t * mt + 32 * rg >= g.R) return;  // a row group without live rows (its partials are not stored)
   const int lane = threadIdx.x & 63, h = threadIdx.x >> 6, l32 = lane & 31, hl = lane >> 5;
   const int row = 32 * rg + l32;  // tile row of this lane
   const long long sf = slot_floats(mt);

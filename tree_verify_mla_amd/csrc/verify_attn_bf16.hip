@@ -772,10 +772,12 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
       // wave w writes 1 KB contiguously, lane l's 16 bytes (features
       // 128 w + 32 fb + 8 gq + 4 (l >> 5) .. +3 of tile row 32 rg + (l & 31))
       // at float offset (((w RG + rg) FB + fb) 4 + gq) 256 + 4 l.
+      // Row groups without a live row are not stored (nothing reads them).
       float* base = p.ws + slot * slot_floats(MT);
       float* ob = base + (size_t)wave * (RG * FB * 4 * 256) + 4 * lane;
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
+      for (int rg = 0; rg < RG; ++rg) {
+        if (t * MT + 32 * rg >= g.R) continue;
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -784,6 +786,7 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
             const f32x4_t v4 = {x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]};
             *reinterpret_cast<f32x4_t*>(ob + ((rg * FB + fb) * 4 + gq) * 256) = v4;
           }
+      }
       if (wave == 0 && hl == 0) {
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {

@@ -61,6 +61,18 @@ __global__ __launch_bounds__(256) void dense_mask_kernel(
 
 }  // namespace
 
+// The bitset and position launch (arguments already checked); also used by
+// ddtree_build_tree_visibility when its tree is too large for the fused builder.
+int ddtree_visibility_launch(const int32_t* node_parents, const int32_t* node_depths,
+                             const int32_t* qo_indptr, const int32_t* prefix_lens, int bs,
+                             int max_q_len, int words_per_row, uint32_t* vis_bits,
+                             int64_t* positions, hipStream_t s) {
+  dim3 grid((max_q_len + 63) / 64, bs);
+  hipLaunchKernelGGL(visibility_kernel, grid, dim3(64), 0, s, node_parents, node_depths,
+                     qo_indptr, prefix_lens, words_per_row, vis_bits, positions);
+  return ddtree::check_launch("compile_visibility");
+}
+
 extern "C" int ddtree_compile_visibility(const int32_t* node_parents, const int32_t* node_depths,
                                          const int32_t* qo_indptr, const int32_t* prefix_lens,
                                          int bs, int max_q_len, int words_per_row,
@@ -83,10 +95,8 @@ extern "C" int ddtree_compile_visibility(const int32_t* node_parents, const int3
                  "compile_visibility: words_per_row %d < ceil(max_q_len/32) for max_q_len %d",
                  words_per_row, max_q_len);
   hipStream_t s = ddtree::as_stream(stream);
-  dim3 grid((max_q_len + 63) / 64, bs);
-  hipLaunchKernelGGL(visibility_kernel, grid, dim3(64), 0, s, node_parents, node_depths,
-                     qo_indptr, prefix_lens, words_per_row, vis_bits, positions);
-  int rc = ddtree::check_launch("compile_visibility");
+  int rc = ddtree_visibility_launch(node_parents, node_depths, qo_indptr, prefix_lens, bs,
+                                    max_q_len, words_per_row, vis_bits, positions, s);
   if (rc != DDTREE_OK || !dense_mask) return rc;
   hipLaunchKernelGGL(dense_mask_kernel, dim3(max_q_len, bs), dim3(256), 0, s, qo_indptr,
                      prefix_lens, vis_bits, words_per_row, mask_indptr, dense_mask);

@@ -1,4 +1,4 @@
-"""One DDTree verify step on device tensors: build -> visibility -> attention -> accept
+"""One DDTree verify step on device tensors: build + visibility -> attention -> accept
 (-> commit of the accepted paths into the KV slot lists).
 
 ``VerifyStep`` owns the output and workspace tensors (torch allocations, made
@@ -91,6 +91,16 @@ class VerifyStep:
                                        x.prefix_lens, x.max_q_len, self.vis_bits,
                                        positions=self.positions, stream=stream)
 
+    def build_visibility(self, stream=None):
+        """build + visibility in one library call (one launch for trees up to
+        64 draft nodes)."""
+        x = self.x
+        _lib.ddtree_build_tree_visibility(x.topk_logprobs, x.topk_ids, x.root_tokens, x.qo_indptr,
+                                          x.prefix_lens, x.max_budget, x.max_q_len,
+                                          self.node_tokens, self.node_parents, self.node_depths,
+                                          self.vis_bits, node_scores=self.node_scores,
+                                          positions=self.positions, stream=stream)
+
     def attention(self, stream=None):
         x = self.x
         _lib.ddtree_verify_attn(x.q, x.kv_pool, x.kv_indptr, x.kv_indices, x.qo_indptr,
@@ -115,7 +125,6 @@ class VerifyStep:
 
     def run(self, stream=None):
         """All four stages (accept needs ``target_predict`` in the inputs)."""
-        self.build(stream)
-        self.visibility(stream)
+        self.build_visibility(stream)
         self.attention(stream)
         self.accept(stream=stream)
