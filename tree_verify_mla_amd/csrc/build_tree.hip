@@ -407,7 +407,8 @@ __global__ __launch_bounds__(64) void build_tree_reg_kernel(
 // one entry per lane.  A pop reads the taken entry with readlane and
 // rewrites only the lanes that change (its slot, and the appended sibling):
 // one select per field, where two frontier entries per lane cost twice the
-// selects and twice the reduction inputs.  The node records (token,
+// selects and twice the reduction inputs.  Each entry keeps its score's
+// order key, formed once when the entry is written.  The node records (token,
 // parent, depth, score) stay in registers too -- node i in lane i & 63,
 // slot i >> 6 -- and go to memory once at the end, as does the optional
 // visibility: node k's ancestor-or-self bitset is its parent's plus bit k,
@@ -471,16 +472,18 @@ __global__ __launch_bounds__(64) void build_lean_kernel(
     for (int w = 0; w < LEAN_WORDS; ++w) n_vis[q][w] = (i >> 5) == w ? 1u << (i & 31) : 0u;
   }
 
-  // the frontier: one entry per lane (meta 0 = empty)
-  uint32_t fs = 0u, fp = 0u, fm = 0u, flo = 0u, fhi = 0u;
+  // the frontier: one entry per lane, with its score's order key (0 = empty)
+  uint32_t fk = 0u, fs = 0u, fp = 0u, fm = 0u, flo = 0u, fhi = 0u;
   if (B > 0 && lane == 0) {  // the root's best child
-    fs = __float_as_uint(__fadd_rn(0.f, __uint_as_float(tl[0])));
+    const float s0 = __fadd_rn(0.f, __uint_as_float(tl[0]));
+    fk = score_key(s0);
+    fs = __float_as_uint(s0);
     fm = pack_meta(1, 0, 0);
   }
   int n = 1;
   for (int k = 1; k <= B; ++k) {
     // 1. the best entry: largest score key, ties resolved exactly
-    const uint32_t key = fm ? score_key(__uint_as_float(fs)) : 0u;
+    const uint32_t key = fk;
     const uint32_t kmax = wave_ext<true>(key);
     if (kmax == 0u) break;  // empty frontier: only reachable if preconditions are broken
     uint64_t hit = __ballot(key == kmax);
@@ -512,17 +515,6 @@ __global__ __launch_bounds__(64) void build_lean_kernel(
       n_dep[q] = (int32_t)wl((uint32_t)n_dep[q], kl, (uint32_t)d);
       n_sc[q] = wl(n_sc[q], kl, __float_as_uint(w_score));
     }
-    if constexpr (VIS) {  // bits of node k = bits of its parent, plus bit k
-#pragma unroll
-      for (int w = 0; w < LEAN_WORDS; ++w) {
-        const uint32_t pv = (p >> 6) == 0 ? lane_val(n_vis[0][w], p & 63)
-                                          : lane_val(n_vis[LEAN_SLOTS - 1][w], p & 63);
-        const uint32_t nv = pv | ((k >> 5) == w ? 1u << (k & 31) : 0u);
-#pragma unroll
-        for (int q = 0; q < LEAN_SLOTS; ++q)
-          if (q == ks) n_vis[q][w] = wl(n_vis[q][w], kl, nv);
-      }
-    }
     if (k == B) break;  // no further pop reads the frontier
 
     // 3. successors: the best child takes slot e, the sibling slot n (or e)
@@ -530,10 +522,12 @@ __global__ __launch_bounds__(64) void build_lean_kernel(
     const float lp_child = __uint_as_float(tab(tl, min(d, D - 1) * K));
     const float lp_sib = __uint_as_float(tab(tl, (d - 1) * K + min(rk + 1, K - 1)));
     const uint64_t cc = code << rank_bits, cs = code + 1;
-    const uint32_t c_s = __float_as_uint(__fadd_rn(w_score, lp_child));
-    const uint32_t s_s = __float_as_uint(__fadd_rn(w_ps, lp_sib));
+    const float c_f = __fadd_rn(w_score, lp_child), s_f = __fadd_rn(w_ps, lp_sib);
+    const uint32_t c_s = __float_as_uint(c_f), s_s = __float_as_uint(s_f);
+    const uint32_t c_k = score_key(c_f), s_k = score_key(s_f);
     const uint32_t c_m = pack_meta(d + 1, 0, k), s_m = pack_meta(d, rk + 1, p);
     if (has_child) {
+      fk = wl(fk, e, c_k);
       fs = wl(fs, e, c_s);
       fp = wl(fp, e, __float_as_uint(w_score));
       fm = wl(fm, e, c_m);
@@ -542,6 +536,7 @@ __global__ __launch_bounds__(64) void build_lean_kernel(
     }
     if (has_sib) {
       const int at = has_child ? n : e;  // n <= k < B <= 64
+      fk = wl(fk, at, s_k);
       fs = wl(fs, at, s_s);
       fp = wl(fp, at, __float_as_uint(w_ps));
       fm = wl(fm, at, s_m);
@@ -549,10 +544,31 @@ __global__ __launch_bounds__(64) void build_lean_kernel(
       fhi = wl(fhi, at, (uint32_t)(cs >> 32));
       n += has_child ? 1 : 0;
     }
-    if (!has_child && !has_sib) fm = wl(fm, e, 0u);
+    if (!has_child && !has_sib) fk = wl(fk, e, 0u);
   }
 
-  // 4. the records (and bitsets, positions) to memory, one store per lane
+  // 4. each node's ancestor-or-self bits: walk up the parent records (at
+  //    most depth_max steps; every node of the wave walks at once)
+  if constexpr (VIS) {
+#pragma unroll
+    for (int q = 0; q < LEAN_SLOTS; ++q) {
+      int j = n_par[q] < lane + 64 * q ? n_par[q] : -1;
+      for (int step = 0; step < D && __ballot(j >= 0); ++step) {
+        if (j >= 0) {
+#pragma unroll
+          for (int w = 0; w < LEAN_WORDS; ++w)
+            if ((j >> 5) == w) n_vis[q][w] |= 1u << (j & 31);
+        }
+        // the parent of j: its record in lane j & 63, slot j >> 6
+        const int src = j >= 0 ? (j & 63) : lane;
+        const int p0 = __shfl(n_par[0], src), p1 = __shfl(n_par[LEAN_SLOTS - 1], src);
+        const int pj = j < 0 ? -1 : ((j >> 6) == 0 ? p0 : p1);
+        j = pj < j ? pj : -1;  // parents precede their children
+      }
+    }
+  }
+
+  // 5. the records (and bitsets, positions) to memory, one store per lane
   const int64_t P = VIS && positions ? (int64_t)max(prefix[r], 0) : 0;
 #pragma unroll
   for (int q = 0; q < LEAN_SLOTS; ++q) {
