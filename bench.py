@@ -39,7 +39,7 @@ FLOP_PER_PAIR = 2 * 576 + 2 * 512  # score dot product + value accumulation per 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=400.0,
                     help="untimed full steps run first, for this long, so that the timed steps "
@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the verify step (no commit, drafter top-k, tree sampling or "
                          "layer-batched lines), e.g. for a trace of the step's kernels alone")
+    ap.add_argument("--ragged-instances", type=int, default=2,
+                    help="instances of the ragged 32-request batch timed among the extras (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -232,8 +234,11 @@ def time_tree_sample(st, wl, K: int, stream, vocab: int = DRAFTER_VOCAB):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    nbytes = wl.total_q * vocab * 4
-    return ms, alen, nbytes
+    # the method reads the target row of every node on the accepted paths
+    # (accept_len rows per request) and the children's probabilities; the
+    # kernels read every node's row to form the block masses beforehand
+    alg = sum(int(o[1].cpu().numpy().sum()) for o in outs) / len(outs) * vocab * 4
+    return ms, alen, alg, wl.total_q * vocab * 4
 
 
 def time_layers(cfg_index: int, L: int, K: int, stream):
@@ -293,19 +298,131 @@ def time_layers(cfg_index: int, L: int, K: int, stream):
             "speedup": round(res[1] / res[0], 3)}
 
 
+def dist_us(ms) -> dict:
+    """Median, 10th and 90th percentile (us) and count of per-call durations (ms)."""
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "mean_us": round(float(a.mean()), 2),
+            "calls": int(a.size)}
+
+
+def attention_modes(steps, stream, n: int) -> dict:
+    """The attention call timed two more ways beside the cold rotation:
+    warm = one instance called back to back (its data stays in the caches);
+    graph = n calls over the rotated instances captured in one HIP graph and
+    replayed (no launch gaps), per call = replay time / n."""
+    import torch
+
+    st = steps[0]
+    for _ in range(20):
+        st.attention(stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        st.attention(stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    warm = dist_us([e[0].elapsed_time(e[1]) for e in ev])
+
+    R = len(steps)
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    with torch.cuda.stream(s):
+        for i in range(R):
+            steps[i].attention(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(n):
+            steps[i % R].attention(s)
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1) / n)
+    del g
+    graph = {"per_call_us": round(float(np.median(reps[1:])) * 1e3, 2), "calls_per_replay": n,
+             "replays": len(reps) - 1}
+    return {"warm": warm, "graph": graph}
+
+
+def ragged_batch_line(instances: int, K: int, stream) -> dict:
+    """The ragged end-to-end workload (32 requests, 64 heads, prefixes
+    1k-32k, budgets 16/32/64): whole verify steps (build + visibility ->
+    attention -> accept) over rotated instances, tree-steps/s from the median
+    step, the attention call against the bf16 MFMA peak, and the histogram of
+    accepted lengths (root included) under the synthetic target predictions."""
+    import torch
+
+    from tree_verify_mla_amd.step import VerifyStep
+    from workloads import draw_target_predict, get_config, make_workload
+    from workloads.device import to_device
+
+    cfg = get_config(5)
+    wls, steps = [], []
+    for k in range(instances):
+        wl = make_workload(cfg, seed=cfg.seed + 1000 * k, unused="zero")
+        st = VerifyStep(to_device(wl, "cuda"))
+        st.build_visibility()
+        torch.cuda.synchronize()
+        tok, par = st.node_tokens.cpu().numpy(), st.node_parents.cpu().numpy()
+        st.x.target_predict = torch.from_numpy(
+            draw_target_predict(wl.seed, tok, par, wl.qo_indptr, wl.vocab)).cuda()
+        wls.append(wl)
+        steps.append(st)
+    flops = [algorithmic_work(w, s.node_depths.cpu().numpy())[0] for w, s in zip(wls, steps)]
+    R = len(steps)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
+        for st in steps:
+            st.run(stream)
+        torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        st = steps[i % R]
+        ev[i][0].record(stream)
+        st.build_visibility(stream)
+        ev[i][1].record(stream)
+        st.attention(stream)
+        ev[i][2].record(stream)
+        st.accept(stream=stream)
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    attn_tflops = [flops[i % R] / (ev[i][1].elapsed_time(ev[i][2]) * 1e-3) / 1e12 for i in range(K)]
+    alen = np.concatenate([st.accept_len.cpu().numpy() for st in steps])
+    hist = {int(v): int(c) for v, c in zip(*np.unique(alen, return_counts=True))}
+    bs = wls[0].bs
+    return {"workload": wls[0].name, "instances": R, "steps": K,
+            "total_q": [w.total_q for w in wls], "step": dist_us(step_ms),
+            "tree_steps_per_s": round(bs / (float(np.median(step_ms)) * 1e-3), 1),
+            "attention_TFLOPs_median": round(float(np.median(attn_tflops)), 1),
+            "mfma_frac_median": round(float(np.median(attn_tflops)) / PEAK_BF16_TFLOPS, 4),
+            "accept_len_histogram": hist, "mean_accept_len": round(float(alen.mean()), 3)}
+
+
 def cpu_baseline(wls, budget_s: float):
     """The CPU oracle as it stands, on whole requests of the workload (cycling
     through the rotated instances) until about budget_s seconds are used."""
     from threadpoolctl import threadpool_info
 
-    from oracle import accept, attention, tree, visibility
+    from oracle import accept, attention, drafter, tree, visibility
     from workloads import draw_target_predict
 
     done, flops, t0 = 0, 0, time.perf_counter()
     for wl in wls:
         for r in range(wl.bs):
             a, b = int(wl.qo_indptr[r]), int(wl.qo_indptr[r + 1])
-            t = tree.build_tree(wl.topk_logprobs[r], wl.topk_ids[r], int(wl.root_tokens[r]), b - a - 1)
+            if wl.drafter_logits is not None:   # the drafter stage first
+                lp, ids = drafter.batch(wl.drafter_logits[r], wl.topk)
+            else:
+                lp, ids = wl.topk_logprobs[r], wl.topk_ids[r]
+            t = tree.build_tree(lp, ids, int(wl.root_tokens[r]), b - a - 1)
             P = int(wl.prefix_lens[r])
             visibility.vis_bits(t.parents, (wl.max_q_len + 31) // 32)
             visibility.positions(t.depths, P)
@@ -409,8 +526,12 @@ def main():
     torch.cuda.synchronize()
     step_ms = t_start.elapsed_time(t_end) / K
     tv_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    attn_calls = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    attn_ms = float(attn_calls.mean())
     acc_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    modes = {"cold": dist_us(attn_calls)}
+    if not args.no_extras:
+        modes.update(attention_modes(steps, stream, max(K, 100)))
 
     extras = None
     if not args.no_extras:
@@ -424,7 +545,9 @@ def main():
         # the drafter's per-depth top-k (the stage before the tree build; not part of a step)
         dk_ms, dk_rows, dk_k, dk_bytes = time_drafter_topk(wls[0], R, K, stream)
         # stochastic acceptance along the tree (the alternative to greedy accept)
-        ts_ms, ts_alen, ts_bytes = time_tree_sample(steps[0], wls[0], K, stream)
+        ts_ms, ts_alen, ts_bytes, ts_read = time_tree_sample(steps[0], wls[0], K, stream)
+        ragged = ragged_batch_line(args.ragged_instances, max(20, K // 5), stream) \
+            if args.ragged_instances > 0 else None
         # one launch over several layers against one launch per layer
         layers = [time_layers(2, 16, K, stream), time_layers(3, 4, max(5, K // 5), stream)]
         extras = {
@@ -443,9 +566,13 @@ def main():
                   "hbm_frac": round(dk_bytes / (dk_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
               "tree_sample": {
                   "vocab": DRAFTER_VOCAB, "us": round(ts_ms * 1e3, 2),
-                  "mean_accept_len": round(ts_alen, 3), "bytes": ts_bytes,
+                  "mean_accept_len": round(ts_alen, 3),
+                  "algorithmic_bytes": round(ts_bytes),
                   "GBps": round(ts_bytes / (ts_ms * 1e-3) / 1e9, 1),
-                  "hbm_frac": round(ts_bytes / (ts_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+                  "hbm_frac": round(ts_bytes / (ts_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                  "kernel_read_bytes": ts_read,
+                  "kernel_read_GBps": round(ts_read / (ts_ms * 1e-3) / 1e9, 1)},
+              "ragged_batch": ragged,
               "verify_attn_layers": layers}
 
     achieved = flops / (attn_ms * 1e-3) / 1e12
@@ -476,6 +603,7 @@ def main():
                      "traffic": None if traffic is None else round(traffic["fetch_bytes"] + traffic["write_bytes"]),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
                      "traffic_detail": traffic},
+        "attention_call": modes,
         "extra": {"attn_ms": round(attn_ms, 5), "build_visibility_ms": round(tv_ms, 5),
                   "accept_ms": round(acc_ms, 5),
                   "attn_GBps": round(gbps, 1), "attn_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),

@@ -7,15 +7,26 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle import accept, attention, tree, visibility
+from oracle import accept, attention, drafter, tree, visibility
 from workloads import draw_target_predict
+
+
+def oracle_tables(wl):
+    """The builder's per-depth top-k tables [bs, D, K] on the oracle side: the
+    workload's drawn tables, or the oracle drafter's top-k of its logits."""
+    if wl.drafter_logits is None:
+        return wl.topk_logprobs, wl.topk_ids
+    bs, D, V = wl.drafter_logits.shape
+    lp, ids = drafter.batch(wl.drafter_logits.reshape(bs * D, V), wl.topk)
+    return lp.reshape(bs, D, wl.topk), ids.reshape(bs, D, wl.topk)
 
 
 class OracleRun:
     def __init__(self, wl):
         self.wl = wl
+        self.topk_logprobs, self.topk_ids = oracle_tables(wl)
         self.trees, self.tokens, self.parents, self.depths, self.scores = tree.build_batch(
-            wl.topk_logprobs, wl.topk_ids, wl.root_tokens, wl.qo_indptr)
+            self.topk_logprobs, self.topk_ids, wl.root_tokens, wl.qo_indptr)
         self.words = (wl.max_q_len + 31) // 32
         self.bits, self.positions, self.dense = visibility.batch(
             self.parents, self.depths, wl.qo_indptr, wl.prefix_lens, self.words)

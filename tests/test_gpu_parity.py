@@ -51,10 +51,21 @@ def _out_f64(st):
 
 
 def _check_integer_stages(orc, st):
+    wl = orc.wl
+    if wl.drafter_logits is not None:
+        # the drafter stage (ddtree_drafter_topk against oracle.drafter): ids
+        # exact, log-probs within 1e-5 (fp32 against fp64, see
+        # tests/test_gpu_drafter.py); the scores built from them then agree to
+        # the same order, the trees exactly (no two candidates within 1e-5)
+        assert np.array_equal(st.x.topk_ids.cpu().numpy(), orc.topk_ids)
+        assert np.abs(st.x.topk_logprobs.cpu().numpy() - orc.topk_logprobs).max() <= 1e-5
+        assert np.abs(st.node_scores.cpu().numpy() - orc.scores).max() <= 1e-5 * (wl.depth + 1)
+    else:
+        assert np.array_equal(st.node_scores.cpu().numpy().view(np.uint32),
+                              orc.scores.view(np.uint32))
     assert np.array_equal(st.node_tokens.cpu().numpy(), orc.tokens)
     assert np.array_equal(st.node_parents.cpu().numpy(), orc.parents)
     assert np.array_equal(st.node_depths.cpu().numpy(), orc.depths)
-    assert np.array_equal(st.node_scores.cpu().numpy().view(np.uint32), orc.scores.view(np.uint32))
     assert np.array_equal(st.vis_bits.cpu().numpy().view(np.uint32), orc.bits)
     assert np.array_equal(st.positions.cpu().numpy(), orc.positions)
     nodes, alen, commit, bonus = orc.accept

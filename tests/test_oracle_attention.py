@@ -184,7 +184,9 @@ def _wrong_masks(par, P):
 
 def _mutation_errors(wl, r, nodes, tol):
     from oracle import tree as tr
-    t = tr.build_tree(wl.topk_logprobs[r], wl.topk_ids[r], int(wl.root_tokens[r]), int(wl.budgets[r]))
+    from tests._oracle_side import oracle_tables
+    lp, ids = oracle_tables(wl)
+    t = tr.build_tree(lp[r], ids[r], int(wl.root_tokens[r]), int(wl.budgets[r]))
     P = int(wl.prefix_lens[r])
     a = int(wl.qo_indptr[r])
     q = wl.q_f32()[a:a + len(t.parents)].astype(np.float64)

@@ -28,8 +28,9 @@ def _request(wl, r, parents):
 def _setup(L=3):
     wl0 = make_workload(get_config(1), bs=2, heads=2, budgets=[6, 3], prefixes=[5, 9],
                         pool_slots=64, dtype="f32")
-    _, _, parents, _, _ = tree.build_batch(wl0.topk_logprobs, wl0.topk_ids, wl0.root_tokens,
-                                           wl0.qo_indptr)
+    from tests._oracle_side import oracle_tables
+    lp, ids = oracle_tables(wl0)
+    _, _, parents, _, _ = tree.build_batch(lp, ids, wl0.root_tokens, wl0.qo_indptr)
     wls = [wl0] + [draw_layer(wl0, l) for l in range(1, L)]
     return wls, parents
 

@@ -20,10 +20,10 @@ def test_deterministic_and_seeded():
     assert not np.array_equal(a.q, c.q)
 
 
-@pytest.mark.parametrize("i", [1, 2])
-def test_shapes_and_preconditions(i):
+@pytest.mark.parametrize("i,drafter", [(1, "tables"), (2, None)])
+def test_shapes_and_preconditions(i, drafter):
     cfg = get_config(i)
-    wl = make_workload(cfg)
+    wl = make_workload(cfg, drafter=drafter)
     Q = cfg.budget + 1
     assert wl.qo_indptr.tolist() == [0, Q]
     assert wl.kv_indptr.tolist() == [0, cfg.prefix + Q]
@@ -51,3 +51,13 @@ def test_ragged_config_draws():
 def test_all_configs_named():
     assert sorted(CONFIGS) == [1, 2, 3, 4, 5]
     assert CONFIGS[3].heads == 64 and CONFIGS[3].bs == 8 and CONFIGS[3].budget == 32 and CONFIGS[3].prefix == 8192
+
+
+def test_tiny_config_draws_drafter_logits():
+    """The tiny configuration's trees start from N(0, 1) drafter logits over
+    the 512-token vocabulary; the tables are left to the method."""
+    wl = make_workload(get_config(1))
+    assert wl.topk_logprobs is None and wl.topk_ids is None
+    assert wl.drafter_logits.shape == (1, 7, 512) and wl.drafter_logits.dtype == np.float32
+    x = wl.drafter_logits.astype(np.float64)
+    assert abs(x.mean()) < 0.1 and abs(x.std() - 1.0) < 0.05

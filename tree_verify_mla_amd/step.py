@@ -36,6 +36,9 @@ class StepInputs:
     max_budget: int
     scale: float
     target_predict: Optional[torch.Tensor] = None  # [total_q] i32
+    # [bs, D, V] f32 drafter logits: when given, the step's drafter stage
+    # (ddtree_drafter_topk) writes topk_logprobs / topk_ids from them
+    drafter_logits: Optional[torch.Tensor] = None
 
     @property
     def bs(self) -> int:
@@ -75,12 +78,32 @@ class VerifyStep:
         self.accept_len = torch.empty(x.bs, **i32)
         self.commit_tokens = torch.empty(x.bs, D + 1, **i32)
         self.bonus_tokens = torch.empty(x.bs, **i32)
+        self.drafter_ws = None
+        if x.drafter_logits is not None:
+            rows = x.drafter_logits.shape[0] * x.drafter_logits.shape[1]
+            self.drafter_ws = torch.empty(max(1, _lib.ddtree_drafter_topk_workspace_size(
+                rows, x.drafter_logits.shape[2], x.topk_logprobs.shape[2])), dtype=torch.uint8,
+                device=dev)
         # the committed slot lists (never longer than the verify lists)
         self.new_kv_indptr = torch.empty(x.bs + 1, **i32)
         self.new_kv_indices = torch.empty(max(x.kv_indices.numel(), 1), **i32)
 
-    def build(self, stream=None):
+    def drafter(self, stream=None):
+        """Per-depth top-k log-probs of the drafter logits (when the inputs
+        carry logits; otherwise the tables are inputs and this does nothing)."""
         x = self.x
+        if x.drafter_logits is None:
+            return
+        bs, D, V = x.drafter_logits.shape
+        K = x.topk_logprobs.shape[2]
+        _lib.ddtree_drafter_topk(x.drafter_logits.view(bs * D, V), x.topk_logprobs.view(bs * D, K),
+                                 x.topk_ids.view(bs * D, K), workspace=self.drafter_ws,
+                                 stream=stream)
+
+    def build(self, stream=None):
+        """The draft trees (after the drafter stage, when the inputs carry logits)."""
+        x = self.x
+        self.drafter(stream)
         _lib.ddtree_build_tree(x.topk_logprobs, x.topk_ids, x.root_tokens, x.qo_indptr,
                                x.max_budget, self.node_tokens, self.node_parents,
                                self.node_depths, self.node_scores, stream=stream)
@@ -93,8 +116,9 @@ class VerifyStep:
 
     def build_visibility(self, stream=None):
         """build + visibility in one library call (one launch for trees up to
-        64 draft nodes)."""
+        64 draft nodes), after the drafter stage when the inputs carry logits."""
         x = self.x
+        self.drafter(stream)
         _lib.ddtree_build_tree_visibility(x.topk_logprobs, x.topk_ids, x.root_tokens, x.qo_indptr,
                                           x.prefix_lens, x.max_budget, x.max_q_len,
                                           self.node_tokens, self.node_parents, self.node_depths,

@@ -36,6 +36,10 @@ class Config:
     depth: int = DEPTH
     vocab: int = VOCAB
     scale: float = SCALE
+    # "logits": the drafter's raw per-depth logits N(0, 1) over the vocabulary
+    # (its log-softmax top-k is a stage of the method); "tables": per-depth
+    # top-k log-prob tables drawn directly
+    drafter: str = "tables"
 
     @property
     def seed(self) -> int:
@@ -44,7 +48,7 @@ class Config:
 
 CONFIGS = {
     1: Config(1, "tiny_fp32_q9_p21", bs=1, heads=8, topk=4, dtype="f32",
-              budget=8, prefix=21, pool_slots=64),
+              budget=8, prefix=21, pool_slots=64, drafter="logits"),
     2: Config(2, "shard8_bf16_q33_p4096", bs=1, heads=8, topk=8, dtype="bf16",
               budget=32, prefix=4096, pool_slots=200_000),
     3: Config(3, "h64_bs8_q33_p8192", bs=8, heads=64, topk=8, dtype="bf16",

@@ -21,9 +21,18 @@ def to_device(wl: Workload, device="cuda", target_predict=None):
     else:
         q = torch.from_numpy(np.ascontiguousarray(wl.q, np.float32)).to(device)
         pool = torch.from_numpy(np.ascontiguousarray(wl.kv_pool, np.float32)).to(device)
+    if wl.drafter_logits is not None:   # the tables are the step's own drafter stage's output
+        bs, D, V = wl.drafter_logits.shape
+        logits = torch.from_numpy(np.ascontiguousarray(wl.drafter_logits, np.float32)).to(device)
+        lp = torch.empty(bs, D, wl.topk, dtype=torch.float32, device=device)
+        ids = torch.empty(bs, D, wl.topk, dtype=torch.int32, device=device)
+    else:
+        logits = None
+        lp = torch.from_numpy(np.ascontiguousarray(wl.topk_logprobs, np.float32)).to(device)
+        ids = _i32(wl.topk_ids, device)
     return StepInputs(
-        topk_logprobs=torch.from_numpy(np.ascontiguousarray(wl.topk_logprobs, np.float32)).to(device),
-        topk_ids=_i32(wl.topk_ids, device),
+        topk_logprobs=lp,
+        topk_ids=ids,
         root_tokens=_i32(wl.root_tokens, device),
         qo_indptr=_i32(wl.qo_indptr, device),
         kv_indptr=_i32(wl.kv_indptr, device),
@@ -37,4 +46,5 @@ def to_device(wl: Workload, device="cuda", target_predict=None):
         max_budget=wl.max_budget,
         scale=float(np.float32(wl.scale)),
         target_predict=None if target_predict is None else _i32(target_predict, device),
+        drafter_logits=logits,
     )

@@ -4,10 +4,13 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order):
 
 1. ragged configs only: per-request prefix lengths ``P_r ~ U{lo..hi}``, then
    per-request budgets ``B_r`` uniform over the allowed choices;
-2. per request r, in request order: the drafter's per-depth top-``k`` table
-   drawn directly (``draw_drafter_topk``: a first log-probability
-   ``-(3 + Exp(1))``, then ``Exp(0.3)`` gaps, rounded to fp32; distinct token
-   ids uniform over the vocabulary); then the root token ``U[0, vocab)``;
+2. per request r, in request order: the drafter's output -- for configs
+   whose drafter is "logits", raw per-depth logits ``N(0, 1)[depth, vocab]``
+   drawn as fp32 (their log-softmax top-k is a stage of the method); for the
+   others the per-depth top-``k`` table drawn directly
+   (``draw_drafter_topk``: a first log-probability ``-(3 + Exp(1))``, then
+   ``Exp(0.3)`` gaps, rounded to fp32; distinct token ids uniform over the
+   vocabulary); then the root token ``U[0, vocab)``;
 3. one permutation of the slot pool: the first ``sum(P_r + Q_r)`` slots are
    dealt out request by request, ``P_r`` prefix slots then ``Q_r`` node slots
    (so ``kv_indices`` is the combined prefix ++ tree-node slot list);
@@ -71,13 +74,14 @@ class Workload:
     prefix_lens: np.ndarray          # [bs] int32
     qo_indptr: np.ndarray            # [bs+1] int32
     kv_indptr: np.ndarray            # [bs+1] int32
-    topk_logprobs: np.ndarray        # [bs, depth, topk] float32
-    topk_ids: np.ndarray             # [bs, depth, topk] int32
+    topk_logprobs: Optional[np.ndarray]  # [bs, depth, topk] float32 (None: from drafter_logits)
+    topk_ids: Optional[np.ndarray]       # [bs, depth, topk] int32 (None: from drafter_logits)
     root_tokens: np.ndarray          # [bs] int32
     kv_indices: np.ndarray           # [sum(P_r+Q_r)] int32
     q: np.ndarray                    # [total_q, H, 576] float32 or uint16 bf16 bits
     kv_pool: np.ndarray              # [num_slots, 576] float32 or uint16 bf16 bits
     extra: dict = field(default_factory=dict)
+    drafter_logits: Optional[np.ndarray] = None  # [bs, depth, vocab] float32 raw logits
 
     # -- derived sizes ------------------------------------------------------
     @property
@@ -167,8 +171,10 @@ def make_workload(cfg: Config, *, seed: Optional[int] = None, unused: str = "nan
                   budgets: Optional[Sequence[int]] = None,
                   prefixes: Optional[Sequence[int]] = None,
                   pool_slots: Optional[int] = None, dtype: Optional[str] = None,
-                  q_std: float = 0.5, kv_std: float = 0.5) -> Workload:
-    """Draw one seeded workload for ``cfg``; keyword overrides shrink or reshape it."""
+                  q_std: float = 0.5, kv_std: float = 0.5,
+                  drafter: Optional[str] = None) -> Workload:
+    """Draw one seeded workload for ``cfg``; keyword overrides shrink or reshape it
+    (``drafter``: "logits" or "tables", see ``Config.drafter``)."""
     seed = cfg.seed if seed is None else int(seed)
     rng = np.random.default_rng(seed)
     bs = cfg.bs if bs is None else int(bs)
@@ -195,12 +201,22 @@ def make_workload(cfg: Config, *, seed: Optional[int] = None, unused: str = "nan
     assert P.shape == (bs,) and B.shape == (bs,)
     Q = B + 1
 
-    # 2. drafter top-k and root tokens
-    lps = np.zeros((bs, D, K), np.float32)
-    ids = np.zeros((bs, D, K), np.int32)
+    # 2. drafter output (raw logits, or top-k tables) and root tokens
+    drafter = cfg.drafter if drafter is None else drafter
+    if drafter not in ("logits", "tables"):
+        raise ValueError(drafter)
+    lps = ids = logits = None
+    if drafter == "logits":
+        logits = np.zeros((bs, D, V), np.float32)
+    else:
+        lps = np.zeros((bs, D, K), np.float32)
+        ids = np.zeros((bs, D, K), np.int32)
     roots = np.zeros(bs, np.int32)
     for r in range(bs):
-        lps[r], ids[r] = draw_drafter_topk(rng, D, K, V)
+        if drafter == "logits":
+            logits[r] = rng.standard_normal((D, V), dtype=np.float32)
+        else:
+            lps[r], ids[r] = draw_drafter_topk(rng, D, K, V)
         roots[r] = rng.integers(0, V)
 
     qo_indptr = np.zeros(bs + 1, np.int32)
@@ -237,7 +253,7 @@ def make_workload(cfg: Config, *, seed: Optional[int] = None, unused: str = "nan
                     scale=cfg.scale, dtype=dtype, budgets=B.astype(np.int64),
                     prefix_lens=P.astype(np.int32), qo_indptr=qo_indptr, kv_indptr=kv_indptr,
                     topk_logprobs=lps, topk_ids=ids, root_tokens=roots, kv_indices=kv_indices,
-                    q=q, kv_pool=pool)
+                    q=q, kv_pool=pool, drafter_logits=logits)
 
 
 def draw_target_predict(seed: int, node_tokens: np.ndarray, node_parents: np.ndarray,
