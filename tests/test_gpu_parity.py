@@ -140,6 +140,19 @@ def test_ragged_edges_bf16():
         _check_attention(orc2, st2)
 
 
+def test_many_requests_bf16():
+    """More requests than the attention kernel's request table holds (64):
+    the schedule falls back to reading the offsets from memory."""
+    _say("test_many_requests_bf16")
+    rng = np.random.default_rng(70)
+    bs = 70
+    wl = make_workload(get_config(3), bs=bs, heads=4, budgets=rng.choice([0, 3, 8, 32], size=bs),
+                       prefixes=rng.integers(0, 300, size=bs), pool_slots=40000)
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st)
+
+
 def test_ragged_edges_fp32():
     _say("test_ragged_edges_fp32")
     wl = make_workload(get_config(1), bs=4, heads=3, budgets=[0, 5, 8, 31], prefixes=[0, 2, 33, 100],

@@ -82,12 +82,13 @@ struct Geom {
   int q0, Q, kv0, N, P, R, T, NB;
 };
 
-__device__ inline Geom geom(const int32_t* qo, const int32_t* kvp, int r, int H, int mt) {
+// geometry of a request from its offsets qo[r], qo[r+1], kvp[r], kvp[r+1]
+__device__ inline Geom geom_of(int q0, int q1, int k0, int k1, int H, int mt) {
   Geom g;
-  g.q0 = qo[r];
-  g.Q = qo[r + 1] - g.q0;
-  g.kv0 = kvp[r];
-  g.N = kvp[r + 1] - g.kv0;
+  g.q0 = q0;
+  g.Q = q1 - q0;
+  g.kv0 = k0;
+  g.N = k1 - k0;
   g.P = g.N - g.Q;
   if (g.Q < 1 || g.P < 0) {
     g.R = g.T = g.NB = 0;
@@ -97,6 +98,10 @@ __device__ inline Geom geom(const int32_t* qo, const int32_t* kvp, int r, int H,
     g.NB = (g.N + KB - 1) / KB;
   }
   return g;
+}
+
+__device__ inline Geom geom(const int32_t* qo, const int32_t* kvp, int r, int H, int mt) {
+  return geom_of(qo[r], qo[r + 1], kvp[r], kvp[r + 1], H, mt);
 }
 
 __device__ inline long long units_of(const Geom& g) { return (long long)g.T * g.NB; }

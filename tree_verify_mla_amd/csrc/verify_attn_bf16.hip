@@ -57,6 +57,8 @@
 //            score MFMAs;
 //   phase B  rare rescale of O; 32 value MFMAs of block b; the softmax of
 //            block b+1 underneath; the first score fragments of block b+2.
+#include <climits>
+
 #include "attn_common.h"
 #include "common.h"
 
@@ -88,7 +90,9 @@ constexpr int SYNC_STEP = 28;      // score step before which the mid-block barr
 constexpr int PBUF = NBUF * BUFB;            // P^T of a block: [row group][k-step] x 1 KB
 constexpr int ABUF = PBUF + RG * 2 * 1024;   // rescale factors [32][RG] f32
 constexpr int SBUF = ABUF + 32 * RG * 4;     // final m, l [2][32][RG] f32
-constexpr int LDS_BYTES = SBUF + 2 * 32 * RG * 4;
+constexpr int TABB = SBUF + 2 * 32 * RG * 4;  // request table: int [4][64], long long [2][64]
+constexpr int TAB_REQ = 64;                  // requests the table holds
+constexpr int LDS_BYTES = TABB + 4 * TAB_REQ * 4 + 2 * TAB_REQ * 8;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(3 * (LPW - 1) + 1 < SYNC_STEP, "gathers are issued before the mid-block barrier");
 constexpr float LN2 = 0.693147180559945309f;
@@ -260,17 +264,98 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
   // of one XCD share a contiguous stretch of work -- for the 64-head batch
   // one request -- and re-read its KV blocks from that XCD's L2 instead of
   // the last-level cache.
-  long long U = 0, Ge = 1, u0 = 0, u1 = 0, v = blockIdx.x;
+  //
+  // With at most TAB_REQ requests, wave 0 first reads every request's offsets
+  // once (one memory round trip) and puts them, with the running sums of the
+  // requests' real and virtual units, in an LDS table; every later lookup
+  // (the range's ends, each segment's request and geometry) is then a table
+  // read and a ballot instead of a chain of dependent global reads.
+  const bool table = p.S == 0 && p.bs <= TAB_REQ;
+  lds_char* const tab_i = lds + TABB;                    // q0, q1, k0, k1 of request r
+  lds_char* const tab_u = lds + TABB + 4 * TAB_REQ * 4;  // inclusive real, virtual units
+  if (table) {
+    if (wave == 0) {
+      const bool in = lane < p.bs;
+      const int q0 = in ? p.qo[lane] : 0, q1 = in ? p.qo[lane + 1] : 0;
+      const int k0 = in ? p.kvp[lane] : 0, k1 = in ? p.kvp[lane + 1] : 0;
+      const Geom gg = geom_of(q0, q1, k0, k1, p.H, MT);
+      long long ui = in ? units_w<false>(gg) : 0, vi = in ? units_w<true>(gg) : 0;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const long long a = shfl_up_ll(ui, d), b = shfl_up_ll(vi, d);
+        if (lane >= d) {
+          ui += a;
+          vi += b;
+        }
+      }
+      lds_st(tab_i + 4 * lane, q0);
+      lds_st(tab_i + 4 * TAB_REQ + 4 * lane, q1);
+      lds_st(tab_i + 8 * TAB_REQ + 4 * lane, k0);
+      lds_st(tab_i + 12 * TAB_REQ + 4 * lane, k1);
+      lds_st(tab_u + 8 * lane, ui);
+      lds_st(tab_u + 8 * TAB_REQ + 8 * lane, vi);
+    }
+    barrier_after<waitcnt_imm(VM_ANY, 0)>();
+  }
+  // geometry of request r (uniform) from the table or from memory
+  auto req_geom = [&](int r) {
+    if (!table) return uniform(geom(p.qo, p.kvp, r, p.H, MT));
+    return uniform(geom_of(lds_ld<int>(tab_i + 4 * r), lds_ld<int>(tab_i + 4 * TAB_REQ + 4 * r),
+                           lds_ld<int>(tab_i + 8 * TAB_REQ + 4 * r),
+                           lds_ld<int>(tab_i + 12 * TAB_REQ + 4 * r), p.H, MT));
+  };
+  // the request whose real (VIRT: virtual) unit range holds unit x and the
+  // units before it (r = bs and the total past the end), as locate()
+  auto req_locate = [&](long long x, bool virt, int& r_out, long long& start_out) {
+    const long long inc = lane < p.bs ? lds_ld<long long>(tab_u + (virt ? 8 * TAB_REQ : 0) + 8 * lane) : 0;
+    const unsigned long long m = __ballot(lane < p.bs && inc > x);
+    const long long tot = shfl_ll(inc, p.bs - 1);
+    if (m == 0) {
+      r_out = p.bs;
+      start_out = tot;
+    } else {
+      const int f = __ffsll((long long)m) - 1;
+      r_out = f;
+      start_out = f == 0 ? 0 : shfl_ll(inc, f - 1);
+    }
+  };
+  long long U = 0, V = 0, Ge = 1, u0 = 0, u1 = 0, v = blockIdx.x;
   if (p.S == 0) {
-    U = uni64(units_before(p.bs, p.qo, p.kvp, p.H, MT));
+    if (table) {
+      int rr;
+      req_locate(LLONG_MAX - 1, false, rr, U);
+      req_locate(LLONG_MAX - 1, true, rr, V);
+      U = uni64(U);
+      V = uni64(V);
+    } else {
+      U = uni64(units_before(p.bs, p.qo, p.kvp, p.H, MT));
+      V = uni64(units_before<true>(p.bs, p.qo, p.kvp, p.H, MT));
+    }
     if (U <= 0) return;
     Ge = effective_groups(U, gridDim.x);
     if (blockIdx.x >= Ge) return;
     if (Ge == gridDim.x && (Ge & 7) == 0) v = (blockIdx.x & 7) * (Ge >> 3) + (blockIdx.x >> 3);
-    // equal shares of the virtual unit list (segment starts cost KAPPA units)
-    const long long V = uni64(units_before<true>(p.bs, p.qo, p.kvp, p.H, MT));
-    u0 = uni64(real_of(range_begin(v, V, Ge), U, p.qo, p.kvp, p.bs, p.H, MT));
-    u1 = uni64(real_of(range_begin(v + 1, V, Ge), U, p.qo, p.kvp, p.bs, p.H, MT));
+    // equal shares of the virtual unit list (segment starts cost KAPPA units);
+    // real_of: the real unit at virtual position x (a position inside a
+    // tile's KAPPA prefix maps to the tile's first unit)
+    auto real_at = [&](long long x) -> long long {
+      if (!table) return uni64(real_of(x, U, p.qo, p.kvp, p.bs, p.H, MT));
+      int r;
+      long long vstart;
+      req_locate(x, true, r, vstart);
+      r = uni(r);
+      if (r >= p.bs) return U;
+      vstart = uni64(vstart);
+      const Geom gr = req_geom(r);
+      const long long local = x - vstart;
+      const long long tt = local / (gr.NB + KAPPA), off = local % (gr.NB + KAPPA);
+      // units of the requests before r: the inclusive sum of r - 1
+      const long long inc = lane < p.bs ? lds_ld<long long>(tab_u + 8 * lane) : 0;
+      const long long ustart = r == 0 ? 0 : shfl_ll(inc, r - 1);
+      return uni64(ustart + tt * gr.NB + (off > KAPPA ? off - KAPPA : 0));
+    };
+    u0 = real_at(range_begin(v, V, Ge));
+    u1 = real_at(range_begin(v + 1, V, Ge));
     if (u0 >= u1) return;  // a share that holds no real unit
   }
 
@@ -279,14 +364,21 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
   // blocks from block 0 onward in step with the rest of its XCD.
   long long cursor = 0;  // next unit among the segments after the first
   bool first_done = false;
+  auto seg_locate = [&](long long u, int& r_out, long long& start_out) {
+    if (table) {
+      req_locate(u, false, r_out, start_out);
+    } else {
+      locate(u, p.qo, p.kvp, p.bs, p.H, MT, r_out, start_out);
+    }
+    r_out = uni(r_out);
+    start_out = uni64(start_out);
+  };
   if (p.S == 0) {
     int r0;
     long long start0;
-    locate(u0, p.qo, p.kvp, p.bs, p.H, MT, r0, start0);
-    r0 = uni(r0);
+    seg_locate(u0, r0, start0);
     if (r0 >= p.bs) return;
-    start0 = uni64(start0);
-    const Geom g0 = uniform(geom(p.qo, p.kvp, r0, p.H, MT));
+    const Geom g0 = req_geom(r0);
     cursor = start0 + min(((u0 - start0) / g0.NB + 1) * g0.NB, u1 - start0);
   }
   int seg_no = 0;
@@ -307,11 +399,9 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
         break;
       }
       long long start;
-      locate(useg, p.qo, p.kvp, p.bs, p.H, MT, r, start);
-      r = uni(r);
+      seg_locate(useg, r, start);
       if (r >= p.bs) break;
-      start = uni64(start);
-      g = uniform(geom(p.qo, p.kvp, r, p.H, MT));
+      g = req_geom(r);
       const long long local = useg - start;
       t = uni((int)(local / g.NB));
       b_begin = uni((int)(local % g.NB));
