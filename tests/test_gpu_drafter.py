@@ -37,8 +37,9 @@ def _gpu(x_dev, k):
     rows, vocab = x_dev.shape
     vals = torch.empty(rows, k, dtype=torch.float32, device="cuda")
     ids = torch.empty(rows, k, dtype=torch.int32, device="cuda")
-    ws = torch.empty(max(_lib.ddtree_drafter_topk_workspace_size(rows, vocab, k), 1),
-                     dtype=torch.uint8, device="cuda")
+    # stale workspace contents must not matter
+    ws = torch.full((max(_lib.ddtree_drafter_topk_workspace_size(rows, vocab, k), 1),), 0x5A,
+                    dtype=torch.uint8, device="cuda")
     _lib.ddtree_drafter_topk(x_dev, vals, ids, workspace=ws)
     torch.cuda.synchronize()
     return vals.cpu().numpy(), ids.cpu().numpy()
@@ -59,7 +60,8 @@ def _dev(x_np, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("vocab,k", [(1, 1), (7, 7), (512, 8), (4097, 16), (8192, 8),
-                                     (8193, 32), (50001, 4), (65536, 16)])
+                                     (8193, 32), (32768, 8), (32769, 16), (50001, 4),
+                                     (65536, 16), (200003, 32)])
 def test_shapes(dtype, vocab, k):
     _say(f"test_shapes {dtype} V={vocab} k={k}")
     rng = np.random.default_rng(vocab * 7 + k)
@@ -94,13 +96,14 @@ def test_ties_and_minus_infinity():
 def test_masked_tail_chunks(dtype):
     _say(f"test_masked_tail_chunks {dtype}")
     rng = np.random.default_rng(14)
-    vocab = 8192 * 4 + 100                         # five chunks, the last one ragged
+    CH = 8192                                      # logits per chunk
+    vocab = CH * 4 + 100                           # five chunks, the last one ragged
     x = draw_drafter_logits(rng, 4, vocab, dtype="f32")
-    x[0, 8192 * 4:] = -np.inf                      # the ragged last chunk
-    x[1, 8192 * 3:] = -np.inf                      # the last two chunks
-    x[2, :8192] = -np.inf                          # the first chunk
-    x[3, 8192:8192 * 2] = -np.inf                  # a middle chunk
-    x[3, 8192 * 4:] = -np.inf
+    x[0, CH * 4:] = -np.inf                        # the ragged last chunk
+    x[1, CH * 3:] = -np.inf                        # the last two chunks
+    x[2, :CH] = -np.inf                            # the first chunk
+    x[3, CH:CH * 2] = -np.inf                      # a middle chunk
+    x[3, CH * 4:] = -np.inf
     if dtype == "bf16":
         from workloads import f32_to_bf16_bits
         xb = f32_to_bf16_bits(x)
@@ -117,3 +120,22 @@ def test_full_size_headline_rows():
         x = draw_drafter_logits(rng, 56, 163840, dtype=dtype)
         xf = bf16_bits_to_f32(x) if dtype == "bf16" else x
         _check(xf, _dev(x, dtype), 8)
+
+
+def test_repeated_calls_on_one_workspace():
+    """One workspace serves call after call, with fewer rows too: whatever a
+    call leaves in it does not matter to the next."""
+    _say("test_repeated_calls_on_one_workspace")
+    rng = np.random.default_rng(15)
+    V, k = 163840, 8
+    ws = torch.empty(_lib.ddtree_drafter_topk_workspace_size(56, V, k), dtype=torch.uint8,
+                     device="cuda")
+    for rows in (56, 56, 7, 56):
+        x = draw_drafter_logits(rng, rows, V, dtype="f32")
+        vals = torch.empty(rows, k, dtype=torch.float32, device="cuda")
+        ids = torch.empty(rows, k, dtype=torch.int32, device="cuda")
+        _lib.ddtree_drafter_topk(torch.from_numpy(x).cuda(), vals, ids, workspace=ws)
+        torch.cuda.synchronize()
+        rv, ri = drafter.batch(x, k)
+        assert np.array_equal(ids.cpu().numpy(), ri)
+        assert np.abs(vals.cpu().numpy() - rv).max() <= TOL

@@ -283,6 +283,83 @@ def test_accept_sentinel_and_full_chain():
     assert st.bonus_tokens.cpu().numpy().tolist() == [-1, 4242]
 
 
+def _accept_case(rng, Q, kind):
+    """(tokens, parents, predictions) of one request.  "bushy": parents among
+    the three previous nodes, three token values, random predictions (many
+    siblings share a token: the smaller index must win).  "deep": mostly a
+    chain; the predictions lead from the root to the last node, whose path
+    carries tokens no other node has.  "star0"/"star1": every node a child of
+    the root, two of them carrying the predicted token, both in the first 64
+    nodes or the first at 64 or beyond."""
+    if kind == "bushy":
+        par = [-1] + [int(rng.integers(max(0, j - 3), j)) for j in range(1, Q)]
+        tok = rng.integers(0, 3, size=Q)
+        pred = rng.integers(0, 3, size=Q)
+    elif kind == "deep":
+        par = [-1] + [j - 1 if rng.random() < 0.7 else int(rng.integers(0, j)) for j in range(1, Q)]
+        tok = rng.integers(0, 8, size=Q)
+        pred = rng.integers(0, 8, size=Q)
+        j, k = Q - 1, 0
+        while j > 0:
+            tok[j] = 1000 + k
+            pred[par[j]] = tok[j]
+            j, k = par[j], k + 1
+    else:
+        par = [-1] + [0] * (Q - 1)
+        tok = rng.integers(0, 6, size=Q)
+        pred = rng.integers(0, 6, size=Q)
+        a, b = (10, 40) if kind == "star0" else (70, 100)
+        tok[a] = tok[b] = pred[0] = 7
+    return (np.asarray(tok, np.int32)[:Q], np.asarray(par, np.int32)[:Q],
+            np.asarray(pred, np.int32)[:Q])
+
+
+def test_accept_random_trees_both_walks():
+    """Requests of 0..300 nodes on both sides of the 128-node register walk,
+    against the oracle bit for bit, at a depth limit the walks never reach
+    and at one that cuts them; an empty request gets the sentinel rows."""
+    _say("test_accept_random_trees_both_walks")
+    from oracle import accept as oacc
+    rng = np.random.default_rng(11)
+    cases = [(1, "bushy"), (2, "deep"), (63, "bushy"), (64, "deep"), (65, "bushy"),
+             (127, "bushy"), (128, "deep"), (0, None), (128, "star0"), (128, "star1"),
+             (129, "deep"), (200, "bushy"), (300, "deep"), (90, "deep")]
+    parts = [_accept_case(rng, Q, kind) if Q else (np.zeros(0, np.int32),) * 3 for Q, kind in cases]
+    sizes = [Q for Q, _ in cases]
+    qo = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    tok, par, pred = (np.concatenate([c[i] for c in parts]) for i in range(3))
+    bs = len(cases)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    reached = 0
+    for D in (300, 5):
+        outs = [torch.full(shape, 77, dtype=torch.int32, device="cuda")
+                for shape in ((bs, D + 1), (bs,), (bs, D + 1), (bs,))]
+        _lib.ddtree_accept(dev(tok), dev(par), dev(qo), dev(pred), D, *outs)
+        torch.cuda.synchronize()
+        nodes, alen, commit, bonus = (t.cpu().numpy() for t in outs)
+        for r, Q in enumerate(sizes):
+            if Q == 0:
+                assert alen[r] == 0 and bonus[r] == -1
+                assert (nodes[r] == -1).all() and (commit[r] == -1).all()
+                continue
+            a, b = qo[r], qo[r + 1]
+            ref = oacc.accept(tok[a:b], par[a:b], pred[a:b], D)
+            case = (D, cases[r])
+            assert alen[r] == ref.accept_len, (case, alen[r], ref.accept_len)
+            assert nodes[r, :ref.accept_len].tolist() == ref.path, case
+            assert (nodes[r, ref.accept_len:] == -1).all(), case
+            assert commit[r, :ref.accept_len].tolist() == ref.commit_tokens, case
+            assert (commit[r, ref.accept_len:] == -1).all(), case
+            assert bonus[r] == ref.bonus, case
+            reached = max(reached, int(nodes[r].max()))
+        if D == 300:
+            star0, star1 = cases.index((128, "star0")), cases.index((128, "star1"))
+            assert nodes[star0, 1] == 10 and nodes[star1, 1] == 70
+    # the walks pass node 64 and node 128, so both register slots and the
+    # walk through memory are exercised
+    assert reached == 299
+
+
 def _graph_replay(wl):
     """The whole step captured in one graph, replayed with eager work between
     the replays; every replay must equal the eager run bit for bit."""

@@ -37,21 +37,49 @@ __global__ __launch_bounds__(64) void accept_kernel(
   }
   int cur = 0, len = 1;
   if (lane == 0) path[0] = 0;
-  while (len < D + 1) {
-    const int t = pred[base + cur];
-    int found = INT_MAX;
-    for (int j = 1 + lane; j < Q; j += 64) {
-      if (par[base + j] == cur && tok[base + j] == t) {
-        found = j;
-        break;  // smallest matching index of this lane's stride
-      }
-    }
+  if (Q <= 128) {
+    // Small trees: parents, tokens and predictions are read once into
+    // registers (node j in lane j & 63, slot j >> 6), so each step is two
+    // ballots instead of a round trip to memory.
+    int p[2], t[2], pr[2];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) found = min(found, __shfl_xor(found, off));
-    if (found == INT_MAX) break;
-    cur = found;
-    if (lane == 0) path[len] = cur;
-    ++len;
+    for (int q = 0; q < 2; ++q) {
+      const int j = lane + 64 * q;
+      const bool in = j < Q;
+      p[q] = in ? par[base + j] : -2;
+      t[q] = in ? tok[base + j] : 0;
+      pr[q] = in ? pred[base + j] : 0;
+    }
+    auto at = [&](const int* v, int j) {  // node j's value, j wave-uniform
+      return __builtin_amdgcn_readlane(j < 64 ? v[0] : v[1], j & 63);
+    };
+    while (len < D + 1) {
+      const int want = at(pr, cur);
+      // children of cur carrying the predicted token; the root is no child
+      const uint64_t m0 = __ballot(lane > 0 && p[0] == cur && t[0] == want);
+      const uint64_t m1 = __ballot(p[1] == cur && t[1] == want);
+      if (!m0 && !m1) break;
+      cur = m0 ? __ffsll((long long)m0) - 1 : 64 + __ffsll((long long)m1) - 1;
+      if (lane == 0) path[len] = cur;
+      ++len;
+    }
+  } else {
+    while (len < D + 1) {
+      const int t = pred[base + cur];
+      int found = INT_MAX;
+      for (int j = 1 + lane; j < Q; j += 64) {
+        if (par[base + j] == cur && tok[base + j] == t) {
+          found = j;
+          break;  // smallest matching index of this lane's stride
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) found = min(found, __shfl_xor(found, off));
+      if (found == INT_MAX) break;
+      cur = found;
+      if (lane == 0) path[len] = cur;
+      ++len;
+    }
   }
   __syncthreads();
   const int b = pred[base + cur];
