@@ -247,22 +247,27 @@ __device__ inline bool merge_plan_fast(const Params& p, int r, int t, const Geom
 // partial in its accumulators' lane layout: wave w's store (rg, fb, gq)
 // writes 1 KB contiguously, lane l's 16 bytes holding features
 // 128 w + 32 fb + 8 gq + 4 (l >> 5) .. +3 of tile row 32 rg + (l & 31).
-// One workgroup per (tile, row group rg, feature quarter w); its wave h reads
-// the runs of fb = 2h, 2h + 1 (8 loads of 1 KB per segment), so lane l folds
-// the segments for its own row with the same ordered log-sum-exp as
+// The 16 runs c = 4 fb + gq of one (tile, row group rg, feature quarter w)
+// are split into 16 / CPW parts of CPW runs; one single-wave workgroup per
+// part reads its runs (CPW loads of 1 KB per segment), so lane l folds the
+// segments for its own row with the same ordered log-sum-exp as
 // merge_kernel, the loads of LANES_BATCH segments issued before any is used.
-// The bf16 output goes through LDS and leaves as 256-byte row segments.
+// The bf16 output goes through LDS and leaves as 16 CPW-byte row segments.
+// CPW = 4 spreads a small merge over twice as many compute units (each one
+// reads at a bounded rate); CPW = 8 keeps larger merges at fewer waves.
 constexpr int LANES_BATCH = 4;
-constexpr int LANES_STR = 256 + 16;  // bytes per staged row (padded: no bank conflicts)
 
-__global__ __launch_bounds__(128) void merge_lanes_kernel(Params p_all, int G) {
+template <int CPW>
+__global__ __launch_bounds__(64) void merge_lanes_kernel(Params p_all, int G) {
+  static_assert(CPW == 4 || CPW == 8, "runs per wave");
   const Params p = at_layer(p_all);
-  constexpr int mt = MT_BF16, RG = 4, FB = 4;
+  constexpr int mt = MT_BF16, RG = 4, FB = 4, NH = 16 / CPW;
+  constexpr int STR = 16 * CPW + 16;  // bytes per staged row (padded)
   typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-  __shared__ __align__(16) char stg[32 * LANES_STR];
-  const int q = blockIdx.x & 15, tile = blockIdx.x >> 4;
-  const int rg = q >> 2, w = q & 3;
+  __shared__ __align__(16) char stg[32 * STR];
+  const int q = blockIdx.x % (16 * NH), tile = blockIdx.x / (16 * NH);
+  const int h = q % NH, rg = (q / NH) >> 2, w = (q / NH) & 3;
   const int r = tile / p.T_max, t = tile % p.T_max;
   if (r >= p.bs) return;
   const Geom g = geom(p.qo, p.kvp, r, p.H, mt);
@@ -270,19 +275,18 @@ __global__ __launch_bounds__(128) void merge_lanes_kernel(Params p_all, int G) {
   MergePlan m;
   if (!merge_plan_fast(p, r, t, g, mt, G, m)) return;
   if (t * mt + 32 * rg >= g.R) return;  // a row group without live rows (its partials are not stored)
-  const int lane = threadIdx.x & 63, h = threadIdx.x >> 6, l32 = lane & 31, hl = lane >> 5;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
   const int row = 32 * rg + l32;  // tile row of this lane
   const long long sf = slot_floats(mt);
-  // chunk c = 4 fb + gq of the wave's runs: c in [8 h, 8 h + 8)
-  const long long run = ((long long)(w * RG + rg) * FB * 4 + 8 * h) * 256 + 4 * lane;
+  const long long run = ((long long)(w * RG + rg) * FB * 4 + CPW * h) * 256 + 4 * lane;
 
   float M = -INFINITY, L = 0.f;
-  float acc[32];
+  float acc[4 * CPW];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 4 * CPW; ++e) acc[e] = 0.f;
   for (long long k0 = 0; k0 < m.nseg; k0 += LANES_BATCH) {
     float ms[LANES_BATCH], ls[LANES_BATCH];
-    float4 x[LANES_BATCH][8];
+    float4 x[LANES_BATCH][CPW];
 #pragma unroll
     for (int j = 0; j < LANES_BATCH; ++j) {
       if (k0 + j < m.nseg) {
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(128) void merge_lanes_kernel(Params p_all, int G) {
         ls[j] = base[(long long)mt * DV + mt + row];
         const float4* src = reinterpret_cast<const float4*>(base + run);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) x[j][c] = src[c * 64];
+        for (int c = 0; c < CPW; ++c) x[j][c] = src[c * 64];
       }
     }
 #pragma unroll
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(128) void merge_lanes_kernel(Params p_all, int G) {
       const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
       const float b = exp2f(ms[j] - Mn);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < CPW; ++c) {
         acc[4 * c] = acc[4 * c] * a + x[j][c].x * b;
         acc[4 * c + 1] = acc[4 * c + 1] * a + x[j][c].y * b;
         acc[4 * c + 2] = acc[4 * c + 2] * a + x[j][c].z * b;
@@ -313,24 +317,24 @@ __global__ __launch_bounds__(128) void merge_lanes_kernel(Params p_all, int G) {
     }
   }
   const float inv = 1.f / L;
-  // chunk c = 8 h + c' holds features 32 fb + 8 gq + 4 hl .. +3 of the quarter
+  // run CPW h + c holds features 8 (CPW h + c) + 4 hl .. +3 of the quarter
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    const int c = 8 * h + cc;
+  for (int c = 0; c < CPW; ++c) {
     bf16x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * cc + e] * inv);
-    *reinterpret_cast<bf16x4*>(stg + l32 * LANES_STR + 2 * (32 * (c >> 2) + 8 * (c & 3) + 4 * hl)) = v;
+    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * c + e] * inv);
+    *reinterpret_cast<bf16x4*>(stg + l32 * STR + 2 * (8 * c + 4 * hl)) = v;
   }
   __syncthreads();
   const size_t row0 = (size_t)g.q0 * p.H + (size_t)t * mt + 32 * rg;  // output row of tile row 32 rg
+  constexpr int RPI = 64 / CPW;  // rows per instruction (CPW lanes of 16 bytes per row)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {  // 16 lanes per row, 4 rows per instruction, 16 rows per wave
-    const int tr = 16 * h + 4 * i + (lane >> 4);
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + tr * LANES_STR + 16 * (lane & 15));
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int tr = RPI * i + lane / CPW, col = lane % CPW;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + tr * STR + 16 * col);
     if (t * mt + 32 * rg + tr < g.R)
       *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + (row0 + tr) * DV + 128 * w +
-                                 8 * (lane & 15)) = v;
+                                 8 * CPW * h + 8 * col) = v;
   }
   if (p.lse && w == 0 && h == 0 && hl == 0 && t * mt + row < g.R)
     p.lse[row0 + l32] = (M + log2f(L)) * LN2;
@@ -345,8 +349,15 @@ int launch_f32(const Params& p, int grid, hipStream_t s) {
 
 int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s) {
   if (mt == MT_BF16) {  // the matrix-core kernel's lane-layout partials (bf16 output)
-    const long long groups = (long long)p.bs * p.T_max * 16;
-    hipLaunchKernelGGL(merge_lanes_kernel, dim3((unsigned)groups, p.L), dim3(128), 0, s, p, grid_groups);
+    // fewer than four waves per compute unit at 8 runs per wave: 4 runs
+    const long long tiles = (long long)p.bs * p.T_max * p.L;
+    if (tiles * 32 < 4LL * device_cu_count()) {
+      hipLaunchKernelGGL(merge_lanes_kernel<4>, dim3((unsigned)(p.bs * p.T_max * 64), p.L), dim3(64),
+                         0, s, p, grid_groups);
+    } else {
+      hipLaunchKernelGGL(merge_lanes_kernel<8>, dim3((unsigned)(p.bs * p.T_max * 32), p.L), dim3(64),
+                         0, s, p, grid_groups);
+    }
     return check_launch("verify_attn(merge)");
   }
   const long long groups = (long long)p.bs * p.T_max * ((mt + MERGE_ROWS - 1) / MERGE_ROWS);
@@ -419,7 +430,7 @@ int verify_attn_impl(const char* fn, int L, const void* q, long long q_ls, const
   const long long T_max = ((long long)max_q_len * num_heads + mt - 1) / mt;
   DDTREE_REQUIRE(T_max * bs * (num_splits > 0 ? num_splits : 1) < (1LL << 31) &&
                      T_max * bs * ((mt + MERGE_ROWS - 1) / MERGE_ROWS) < (1LL << 31) &&
-                     T_max * bs * 16 < (1LL << 31),
+                     T_max * bs * 64 < (1LL << 31),
                  DDTREE_EUNSUPPORTED, "%s: grid too large", fn);
 
   const long long esz = dtype == DDTREE_BF16 ? 2 : 4;
