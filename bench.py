@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector ALUs (the fp32 path is not a matrix-core kernel)
 FLOP_PER_PAIR = 2 * 576 + 2 * 512  # score dot product + value accumulation per (row, column)
 
 
@@ -576,6 +577,8 @@ def main():
               "verify_attn_layers": layers}
 
     achieved = flops / (attn_ms * 1e-3) / 1e12
+    bf16 = wls[0].dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     traffic = measured_traffic(wls[0].name)
     value = flops / (step_ms * 1e-3) / 1e12
     gbps = nbytes / (attn_ms * 1e-3) / 1e9
@@ -592,14 +595,18 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wls[0].dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; random latents, drawn drafter top-k tables)",
+        "data": "synthetic (seeded; random latents, " + (
+            "drafter top-k from N(0,1) logits)" if wls[0].drafter_logits is not None
+            else "drawn drafter top-k tables)"),
         "config": {"workload": wls[0].name, "bs": wls[0].bs, "heads": wls[0].heads,
                    "q_len": int(wls[0].max_q_len), "prefix": int(wls[0].prefix_lens.max()),
                    "topk": wls[0].topk, "pool_slots": wls[0].num_slots, "instances": R,
                    "num_splits": args.num_splits, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "ddtree_verify_attn (attn_bf16_kernel + merge_lanes_kernel)",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma" if bf16 else "alu",
+                     "kernel": "ddtree_verify_attn (attn_bf16_kernel + merge_lanes_kernel)" if bf16
+                     else "ddtree_verify_attn (attn_f32_kernel)",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
                      "traffic": None if traffic is None else round(traffic["fetch_bytes"] + traffic["write_bytes"]),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
                      "traffic_detail": traffic},
