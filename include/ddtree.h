@@ -211,7 +211,10 @@ size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int max_q_len, i
  *              bytes (may be NULL when that is 0).
  * Arithmetic: bf16 inputs use bf16 matrix cores with fp32 accumulation, the
  * softmax weights rounded to bf16 for the value product, output rounded to
- * bf16; f32 inputs compute in fp32 throughout.
+ * bf16; f32 inputs compute in fp32 throughout, on a vector-ALU kernel meant
+ * for small batches and for checking the bf16 path: each of its query rows
+ * reads its request's KV rows itself, so its time grows as H * Q * N (any
+ * size is accepted and correct).
  * Errors: EINVAL (null required pointer, bs < 0, num_heads < 1, max_q_len < 1,
  * max_kv_len < max_q_len, words_per_row too small, non-finite scale,
  * num_slots < 1, num_splits < 0, bad dtype); EWORKSPACE.  A pool index
