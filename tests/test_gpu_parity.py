@@ -153,6 +153,18 @@ def test_many_requests_bf16():
     _check_attention(orc, st)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_trees_past_128_nodes(dtype):
+    """Trees of more than 128 nodes: the attention reads the rows' ancestor
+    words past the fourth from memory in its tail blocks (W = 7 here)."""
+    _say(f"test_trees_past_128_nodes {dtype}")
+    wl = make_workload(get_config(3), bs=3, heads=2, budgets=[200, 129, 3], prefixes=[50, 0, 700],
+                       pool_slots=5000, dtype=dtype)
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st)
+
+
 def test_ragged_edges_fp32():
     _say("test_ragged_edges_fp32")
     wl = make_workload(get_config(1), bs=4, heads=3, budgets=[0, 5, 8, 31], prefixes=[0, 2, 33, 100],
