@@ -242,6 +242,47 @@ def time_tree_sample(st, wl, K: int, stream, vocab: int = DRAFTER_VOCAB):
     return ms, alen, alg, wl.total_q * vocab * 4
 
 
+def measured_peaks(stream) -> dict:
+    """The device's own side of the roofline ratios: compute units and peak
+    clock as the runtime reports them, the rate of a loop of nothing but
+    bf16 32x32x16 matrix-core instructions (one workgroup of four waves per
+    compute unit, eight independent accumulators per wave), and the rate of
+    a 512 MiB device-to-device copy (bytes read + written).  Medians of 10
+    timed launches after 3 untimed."""
+    import torch
+    from tree_verify_mla_amd import _lib
+
+    cus, khz = _lib.ddtree_device_info()
+    grid = cus
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+
+    def med(fn, n=10):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    flops = grid * 4 * 4096 * 8 * 32768
+    t_mfma = med(lambda: _lib.ddtree_probe_mfma_loop(grid, 4096, out, stream=stream))
+    src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = med(lambda: dst.copy_(src))
+    copy_bytes = 2 * src.numel() * 4
+    del src, dst
+    mfma = flops / t_mfma / 1e12
+    copy = copy_bytes / t_copy / 1e9
+    return {"compute_units": cus, "peak_clock_MHz": round(khz / 1e3),
+            "mfma_bf16_loop_TFLOPs": round(mfma, 1), "mfma_loop_frac_of_published": round(mfma / PEAK_BF16_TFLOPS, 4),
+            "copy_GBps": round(copy, 1), "copy_frac_of_published": round(copy / PEAK_HBM_GBPS, 4)}
+
+
 def time_layers(cfg_index: int, L: int, K: int, stream):
     """ddtree_verify_attn_layers over L layers (seeded latents per layer, one
     slot list) against L back-to-back ddtree_verify_attn calls: average ms of
@@ -551,7 +592,9 @@ def main():
             if args.ragged_instances > 0 else None
         # one launch over several layers against one launch per layer
         layers = [time_layers(2, 16, K, stream), time_layers(3, 4, max(5, K // 5), stream)]
+        peaks = measured_peaks(stream)
         extras = {
+              "measured_peaks": peaks,
               "commit_kv": {
                   "index_form_us": round(commit_i_ms * 1e3, 2),
                   "index_form_bytes": round(cb_i),

@@ -14,6 +14,8 @@
  *   ddtree_tree_sample         (or) stochastic acceptance against the target distribution
  *   ddtree_commit_kv           the accepted path into the KV cache (after accept)
  *   ddtree_validate_inputs     (debug) checks the index arrays a step is built from
+ *   ddtree_probe_mfma_loop, ddtree_device_info  (measurement) the device's sustained
+ *                              matrix-core rate and its compute units and clock
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -480,6 +482,25 @@ int ddtree_validate_inputs(int bs, const int32_t* qo_indptr, int total_q,
                            const int32_t* kv_indptr, const int32_t* kv_indices,
                            int64_t num_kv_indices, int64_t num_slots, const int32_t* prefix_lens,
                            const int32_t* node_parents, int32_t* report, void* stream);
+
+/*
+ * Measurement probes (not a stage of the method).  A roofline fraction is a
+ * measured rate over a published peak; these give the device's own side of
+ * that ratio.
+ *
+ * ddtree_probe_mfma_loop -- grid workgroups of 256 threads; each wave runs
+ * iters rounds of 8 independent v_mfma_f32_32x32x16_bf16 (32768 flops each)
+ * and writes one float per thread to out [grid * 256] (the accumulators'
+ * sum, so the loop is not removed).  Flops per launch =
+ * grid * 4 * iters * 8 * 32768.  Errors: EINVAL (grid < 1, iters < 1, null
+ * out).
+ *
+ * ddtree_device_info -- the current device's compute-unit count and peak
+ * shader clock in kHz, as the runtime reports them.  Errors: EINVAL (null
+ * pointer), EHIP (no device or the query failed).
+ */
+int ddtree_probe_mfma_loop(int grid, int iters, float* out, void* stream);
+int ddtree_device_info(int* compute_units, int* peak_clock_khz);
 
 #ifdef __cplusplus
 }

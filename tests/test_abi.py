@@ -258,3 +258,12 @@ def test_build_tree_visibility_validation(lib):
     assert f(*a) == EINVAL
     assert call(9, 0) == EINVAL                     # max_q_len
     assert call(5, 0) == 0                          # empty batch
+
+
+def test_measurement_probes_reject_bad_arguments(lib):
+    f = lib.ddtree_probe_mfma_loop
+    assert f(0, 1, FAKE, NULL) == EINVAL
+    assert f(1, 0, FAKE, NULL) == EINVAL
+    assert f(1, 1, NULL, NULL) == EINVAL
+    assert "probe_mfma_loop" in _err(lib)
+    assert lib.ddtree_device_info(NULL, NULL) == EINVAL

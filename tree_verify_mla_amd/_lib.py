@@ -77,6 +77,10 @@ def load() -> ctypes.CDLL:
     lib.ddtree_tree_sample_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, P, P, P]
     lib.ddtree_validate_inputs.restype = I
     lib.ddtree_validate_inputs.argtypes = [I, P, I, P, P, I64, I64, P, P, P, P]
+    lib.ddtree_probe_mfma_loop.restype = I
+    lib.ddtree_probe_mfma_loop.argtypes = [I, I, P, P]
+    lib.ddtree_device_info.restype = I
+    lib.ddtree_device_info.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     _lib = lib
     return lib
 
@@ -331,3 +335,19 @@ def ddtree_tree_sample_noalloc(node_tokens, node_parents, qo_indptr, target_prob
         _p(accepted_nodes, torch.int32, "accepted_nodes"),
         _p(accept_len, torch.int32, "accept_len"), _p(commit_tokens, torch.int32, "commit_tokens"),
         _p(bonus_tokens, torch.int32, "bonus_tokens"), _stream(stream)))
+
+
+def ddtree_probe_mfma_loop(grid: int, iters: int, out, stream=None) -> int:
+    """Launch the matrix-core loop probe; returns its flops per launch."""
+    if out.numel() < grid * 256:
+        raise ValueError("out must hold grid * 256 floats")
+    _check("ddtree_probe_mfma_loop", load().ddtree_probe_mfma_loop(
+        int(grid), int(iters), _p(out, torch.float32, "out"), _stream(stream)))
+    return grid * 4 * iters * 8 * 32768
+
+
+def ddtree_device_info():
+    """(compute units, peak shader clock in kHz) of the current device."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    _check("ddtree_device_info", load().ddtree_device_info(ctypes.byref(cus), ctypes.byref(khz)))
+    return cus.value, khz.value
