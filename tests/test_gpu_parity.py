@@ -165,6 +165,19 @@ def test_trees_past_128_nodes(dtype):
     _check_attention(orc, st)
 
 
+def test_maximum_budget_end_to_end():
+    """The largest tree the builder takes (2048 draft nodes, 2049-node rows of
+    65 bitset words), a mid-size one and an autoregressive request, through
+    the whole step: the LDS-frontier builder, bitsets and positions, the
+    attention's mask from ancestor words in memory, and accept."""
+    _say("test_maximum_budget_end_to_end")
+    wl = make_workload(get_config(3), bs=3, heads=2, depth=8, topk=32, budgets=[2048, 1000, 0],
+                       prefixes=[0, 100, 7], pool_slots=5000, seed=2048)
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st)
+
+
 def test_ragged_edges_fp32():
     _say("test_ragged_edges_fp32")
     wl = make_workload(get_config(1), bs=4, heads=3, budgets=[0, 5, 8, 31], prefixes=[0, 2, 33, 100],
