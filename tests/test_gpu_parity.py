@@ -178,6 +178,18 @@ def test_maximum_budget_end_to_end():
     _check_attention(orc, st)
 
 
+def test_pool_past_4gib():
+    """A bf16 pool of 5M slots (5.8 GB): byte offsets past 2^32 take the
+    kernel's 64-bit global gathers instead of the buffer-resource ones."""
+    _say("test_pool_past_4gib")
+    wl = make_workload(get_config(3), bs=2, heads=4, budgets=[32, 16], prefixes=[3000, 500],
+                       pool_slots=5_000_000)
+    assert int(wl.kv_indices.max()) * 1152 > 2 ** 32  # some rows lie past the first 4 GiB
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st)
+
+
 def test_ragged_edges_fp32():
     _say("test_ragged_edges_fp32")
     wl = make_workload(get_config(1), bs=4, heads=3, budgets=[0, 5, 8, 31], prefixes=[0, 2, 33, 100],
