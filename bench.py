@@ -661,7 +661,11 @@ def main():
                   **(extras or {})},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wls, args.cpu_seconds)
+        cb = cpu_baseline(wls, args.cpu_seconds)
+        # the same step on the GPU against the oracle on the host cores
+        cb["gpu_speedup"] = {"flops_rate": round(value / cb["value"], 1),
+                             "tree_steps": round(line["extra"]["tree_steps_per_s"] / cb["tree_steps_per_s"], 1)}
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 
