@@ -1,8 +1,10 @@
 // ddtree_accept: greedy root walk along the target argmax, one wavefront per
-// request.  Each step the lanes scan the request's nodes for a child of the
-// current node whose token equals the target's prediction there; a wave
-// minimum picks the smallest such index ("The DDTree CUDA Graph Fix ...",
-// section "The DDTree Architecture: Confirming Multiple-Path Evaluation").
+// request.  Each step the lanes look among the request's nodes for a child of
+// the current node whose token equals the target's prediction there, and the
+// smallest such index wins ("The DDTree CUDA Graph Fix ...", section "The
+// DDTree Architecture: Confirming Multiple-Path Evaluation"): for trees of up
+// to 128 nodes over registers loaded once (two ballots a step), for larger
+// ones by a scan of memory and a wave minimum.
 // The walk ends when no child matches or after depth_max + 1 path nodes; the
 // bonus is the prediction at the last accepted node ("The Oracle Drafter
 // ...", sections "The Engine Interface Design" and "Reasoning About Cache
