@@ -295,6 +295,43 @@ __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __
   }
   const float lse = M + __logf(S);
 
+  if (C <= 64) {
+    // Each chunk wrote its candidates best first, so the row's k best are a
+    // merge of C sorted lists: lane c follows chunk c's list, and a round
+    // takes the best head (the largest key, then the smallest id) and moves
+    // the winner's head along -- one LDS read, where the general path below
+    // may rescan a lane's candidates.
+    __shared__ uint32_t s_key[64 * MERGE_PER_LANE], s_id[64 * MERGE_PER_LANE];
+    __shared__ float s_val[64 * MERGE_PER_LANE];
+#pragma unroll
+    for (int q = 0; q < MERGE_PER_LANE; ++q) {
+      const int i = lane + 64 * q;
+      if (i < nc) {
+        s_key[i] = key[q];
+        s_id[i] = id[q];
+        s_val[i] = val[q];
+      }
+    }
+    __syncthreads();
+    const int base = lane * k;
+    int pos = 0;
+    uint32_t hk = lane < C ? s_key[base] : 0u, hid = lane < C ? s_id[base] : 0xffffffffu;
+    float hv = lane < C ? s_val[base] : 0.f;
+    for (int r = 0; r < k; ++r) {
+      const uint32_t gk = wave_ext<true>(hk);
+      const uint32_t gid = wave_ext<false>(hk == gk ? hid : 0xffffffffu);
+      if (gk != 0u && hk == gk && hid == gid) {
+        out_val[(size_t)row * k + r] = hv - lse;
+        out_id[(size_t)row * k + r] = (int32_t)gid;
+        ++pos;
+        hk = pos < k ? s_key[base + pos] : 0u;
+        hid = pos < k ? s_id[base + pos] : 0xffffffffu;
+        hv = pos < k ? s_val[base + pos] : 0.f;
+      }
+    }
+    return;
+  }
+
   // a lane's two best candidates after (lk, lid) in (key descending, id
   // ascending) order; lk = ~0u: from the top (ids are unique)
   auto best_two = [&](uint32_t lk, uint32_t lid, uint32_t& k1, uint32_t& i1, float& v1,
