@@ -37,6 +37,10 @@ __device__ inline uint32_t fkey(float f) {
   const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);  // -0 ties with +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// its inverse (key 0x80000000u gives +0)
+__device__ inline float funkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 __device__ inline float wave_max_f(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -102,7 +106,6 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
                                                    int32_t* __restrict__ ws_id) {
   __shared__ float red_f[CT / 64];
   __shared__ uint2 cand[CT / 64][KMAX];   // each wave's k best: (key, id)
-  __shared__ float cand_v[CT / 64][KMAX]; // and their logits
   const int row = blockIdx.x / C, c = blockIdx.x % C;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const long long c0 = (long long)c * CHUNK;          // first element of the chunk in its row
@@ -178,29 +181,27 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
   //    waits for it.
   // 2. after one barrier, wave 0 takes the chunk's k best out of the 4 k
   //    wave candidates in LDS the same way.
+  // The keys take the logits' place (a key gives its logit back), which
+  // keeps the kernel within the registers of five waves per SIMD.
   uint32_t key[EPT];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) key[j] = ((live >> j) & 1u) ? fkey(x[j]) : 0u;
   // the two best entries after (bk, bj) in the order; bk = ~0u: from the top
-  auto best_two = [&](uint32_t lk, int lj, uint32_t& k1, int& j1, float& x1, uint32_t& k2,
-                      int& j2, float& x2) {
-    k1 = 0u, j1 = 0, x1 = 0.f, k2 = 0u, j2 = 0, x2 = 0.f;
+  auto best_two = [&](uint32_t lk, int lj, uint32_t& k1, int& j1, uint32_t& k2, int& j2) {
+    k1 = 0u, j1 = 0, k2 = 0u, j2 = 0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const uint32_t kj = (key[j] < lk || (key[j] == lk && j > lj)) ? key[j] : 0u;
       const bool first = kj > k1, second = !first && kj > k2;
       k2 = first ? k1 : (second ? kj : k2);
       j2 = first ? j1 : (second ? j : j2);
-      x2 = first ? x1 : (second ? x[j] : x2);
       k1 = first ? kj : k1;
       j1 = first ? j : j1;
-      x1 = first ? x[j] : x1;
     }
   };
   uint32_t k1, k2;
   int j1, j2;
-  float x1, x2;
-  best_two(0xffffffffu, -1, k1, j1, x1, k2, j2, x2);
+  best_two(0xffffffffu, -1, k1, j1, k2, j2);
   for (int r = 0; r < k; ++r) {
     const uint32_t myid = k1 ? (uint32_t)(c0 + elem_of_rt<T, VEC>(t, j1)) : 0xffffffffu;
     const uint32_t wk = wave_ext<true>(k1);
@@ -209,11 +210,10 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
       if (lane == 0) cand[wave][r] = make_uint2(0u, 0xffffffffu);
     } else if (k1 == wk && myid == wid) {  // the owner
       cand[wave][r] = make_uint2(wk, wid);
-      cand_v[wave][r] = x1;
       if (k2 != 0u) {
-        k1 = k2, j1 = j2, x1 = x2, k2 = 0u;
+        k1 = k2, j1 = j2, k2 = 0u;
       } else {
-        best_two(k1, j1, k1, j1, x1, k2, j2, x2);
+        best_two(k1, j1, k1, j1, k2, j2);
       }
     }
   }
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
     ck[q] = 0u, cid[q] = 0xffffffffu, cv[q] = 0.f;
     if (i < (CT / 64) * k) {
       const uint2 v = cand[i / k][i % k];
-      ck[q] = v.x, cid[q] = v.y, cv[q] = cand_v[i / k][i % k];
+      ck[q] = v.x, cid[q] = v.y, cv[q] = funkey(v.x);
     }
   }
   for (int r = 0; r < k; ++r) {
