@@ -254,12 +254,12 @@ __device__ inline bool merge_plan_fast(const Params& p, int r, int t, const Geom
 // merge_kernel, the loads of LANES_BATCH segments issued before any is used.
 // The bf16 output goes through LDS and leaves as 16 CPW-byte row segments.
 // CPW = 4 spreads a small merge over twice as many compute units (each one
-// reads at a bounded rate); CPW = 8 keeps larger merges at fewer waves.
-constexpr int LANES_BATCH = 4;
-
-template <int CPW>
+// reads at a bounded rate); CPW = 8 keeps larger merges at fewer waves; the
+// smallest merges (fewer than 8 tiles) take CPW = 2 with 8 segments' loads
+// in flight.
+template <int CPW, int LANES_BATCH>
 __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p_all, int G) {
-  static_assert(CPW == 4 || CPW == 8, "runs per wave");
+  static_assert(CPW == 2 || CPW == 4 || CPW == 8, "runs per wave");
   const Params p = at_layer(p_all);
   constexpr int mt = MT_BF16, RG = 4, FB = 4, NH = 16 / CPW;
   constexpr int STR = 16 * CPW + 16;  // bytes per staged row (padded)
@@ -349,13 +349,18 @@ int launch_f32(const Params& p, int grid, hipStream_t s) {
 
 int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s) {
   if (mt == MT_BF16) {  // the matrix-core kernel's lane-layout partials (bf16 output)
-    // fewer than four waves per compute unit at 8 runs per wave: 4 runs
+    // fewer than four waves per compute unit at 8 runs per wave: 4 runs; at
+    // 4 runs: 2
     const long long tiles = (long long)p.bs * p.T_max * p.L;
-    if (tiles * 32 < 4LL * device_cu_count()) {
-      hipLaunchKernelGGL(merge_lanes_kernel<4>, dim3((unsigned)(p.bs * p.T_max * 64), p.L), dim3(64),
+    const long long cus = device_cu_count();
+    if (tiles * 128 < 4LL * cus) {
+      hipLaunchKernelGGL((merge_lanes_kernel<2, 8>), dim3((unsigned)(p.bs * p.T_max * 128), p.L),
+                         dim3(64), 0, s, p, grid_groups);
+    } else if (tiles * 32 < 4LL * cus) {
+      hipLaunchKernelGGL((merge_lanes_kernel<4, 4>), dim3((unsigned)(p.bs * p.T_max * 64), p.L), dim3(64),
                          0, s, p, grid_groups);
     } else {
-      hipLaunchKernelGGL(merge_lanes_kernel<8>, dim3((unsigned)(p.bs * p.T_max * 32), p.L), dim3(64),
+      hipLaunchKernelGGL((merge_lanes_kernel<8, 4>), dim3((unsigned)(p.bs * p.T_max * 32), p.L), dim3(64),
                          0, s, p, grid_groups);
     }
     return check_launch("verify_attn(merge)");
