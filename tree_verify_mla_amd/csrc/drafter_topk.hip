@@ -12,15 +12,16 @@
 // Two kernels, in the shape of a vocabulary split across ranks:
 // * chunk_kernel: workgroup (row, chunk) reads CHUNK consecutive logits of
 //   its row once (32 per thread, kept in registers) and writes the chunk's
-//   max m_c, its sum s_c of e^(x - m_c), and its k best (value, id) by k
-//   rounds of a workgroup argmax over the entries still in play (32-bit
+//   max m_c, its sum s_c of e^(x - m_c), and its k best (value, id), best
+//   first, by rounds of an argmax over the entries still in play (32-bit
 //   order keys, the smallest id among equal keys);
-// * merge_kernel: one wavefront per row folds the chunks in chunk order,
-//   M = max m_c, S = sum_c s_c e^(m_c - M), lse = M + log S, and takes the
-//   row's k best out of the chunks' candidates (the j-th best of a row is
-//   among the j best of its chunk), writing x - lse and the ids.
+// * merge_kernel: one wavefront per row folds the chunks' (m_c, s_c) into
+//   M = max m_c and S = sum_c s_c e^(m_c - M), lse = M + log S, and takes
+//   the row's k best out of the chunks' candidates (the j-th best of a row
+//   is among the j best of its chunk), writing x - lse and the ids.
 // Everything is fp32; exponentials and the log are the hardware's.
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 
@@ -40,16 +41,6 @@ __device__ inline uint32_t fkey(float f) {
 // its inverse (key 0x80000000u gives +0)
 __device__ inline float funkey(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-__device__ inline float wave_max_f(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ inline float wave_sum_f(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
 }
 
 // element e (0 <= e < CHUNK) of the chunk sits in thread t, register j:
@@ -93,6 +84,41 @@ __device__ inline uint32_t wave_ext(uint32_t x) {
   return op(op(r0, r1), op(r2, r3));
 }
 
+// (m, s) <- (m, s) + (m2, s2): a pair is a max and a sum of e^(x - max); a
+// max of -inf carries no mass
+__device__ inline void lse_add(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  const float a = m == -INFINITY ? 0.f : s * __expf(m - M);
+  const float b = m2 == -INFINITY ? 0.f : s2 * __expf(m2 - M);
+  m = M;
+  s = a + b;
+}
+
+// the wave's (m, s) in every lane: inside each 16-lane row by DPP (both
+// partners of a step form the same sum), then the four rows in order
+__device__ inline void wave_lse(float& m, float& s) {
+  auto step = [&](auto ctrl) {
+    const float m2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), ctrl.value, 0xF, 0xF, false));
+    const float s2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), ctrl.value, 0xF, 0xF, false));
+    lse_add(m, s, m2, s2);
+  };
+  step(std::integral_constant<int, 0xB1>{});
+  step(std::integral_constant<int, 0x4E>{});
+  step(std::integral_constant<int, 0x141>{});
+  step(std::integral_constant<int, 0x140>{});
+  float r_m[4], r_s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r_m[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16 * i));
+    r_s[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 16 * i));
+  }
+  lse_add(r_m[0], r_s[0], r_m[1], r_s[1]);
+  lse_add(r_m[2], r_s[2], r_m[3], r_s[3]);
+  lse_add(r_m[0], r_s[0], r_m[2], r_s[2]);
+  m = r_m[0];
+  s = r_s[0];
+}
+
 template <typename T>
 __device__ inline float to_f32(T x) {
   if constexpr (sizeof(T) == 2) return (float)x;
@@ -104,7 +130,7 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
                                                    int k, float* __restrict__ ws_ms,
                                                    float* __restrict__ ws_val,
                                                    int32_t* __restrict__ ws_id) {
-  __shared__ float red_f[CT / 64];
+  __shared__ float red_m[CT / 64], red_s[CT / 64];
   __shared__ uint2 cand[CT / 64][KMAX];   // each wave's k best: (key, id)
   const int row = blockIdx.x / C, c = blockIdx.x % C;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -141,32 +167,26 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
   for (int j = 0; j < EPT; ++j)
     if (elem_of<T, VEC>(t, j) < n) live |= 1u << j;
 
-  // chunk max and sum of e^(x - max)
+  // The chunk's max m and sum s of e^(x - m): each lane's own (max, sum)
+  // first, then the wave's and the workgroup's by the pairwise rule
+  // (m, s) + (m', s') = (M, s e^(m - M) + s' e^(m' - M)), M = max(m, m'), so
+  // the workgroup meets at one barrier only.  Elements with nothing in them
+  // (a masked tail of the vocabulary) give max -inf and sum 0, which the
+  // merge skips; their reference is 0, so e^(-inf - 0) = 0.
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) m = fmaxf(m, x[j]);
-  m = wave_max_f(m);
-  if (lane == 0) red_f[wave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-  __syncthreads();
-  // A chunk of nothing but -inf (a masked tail of the vocabulary) has no
-  // mass: its sum is 0 and its max stays -inf, which the merge skips.  The
-  // reference then is 0, so e^(-inf - 0) = 0 rather than e^(-inf + inf).
   const float mref = m == -INFINITY ? 0.f : m;
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < EPT; ++j)
     if ((live >> j) & 1u) s += __expf(x[j] - mref);
-  s = wave_sum_f(s);
-  if (lane == 0) red_f[wave] = s;
-  __syncthreads();
-  s = (red_f[0] + red_f[1]) + (red_f[2] + red_f[3]);
-  const size_t slot = (size_t)row * C + c;
-  if (t == 0) {
-    ws_ms[2 * slot] = m;
-    ws_ms[2 * slot + 1] = s;
+  wave_lse(m, s);
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_s[wave] = s;
   }
+  const size_t slot = (size_t)row * C + c;
 
   // The chunk's k best (the largest value, then the smallest id), in two
   // steps without a barrier per round.  Keys are 32-bit order keys; 0 means
@@ -219,6 +239,14 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
   }
   __syncthreads();
   if (wave != 0) return;
+  if (t == 0) {  // the workgroup's (max, sum), waves in order
+    float mc = red_m[0], sc = red_s[0];
+    lse_add(mc, sc, red_m[1], red_s[1]);
+    lse_add(mc, sc, red_m[2], red_s[2]);
+    lse_add(mc, sc, red_m[3], red_s[3]);
+    ws_ms[2 * slot] = mc;
+    ws_ms[2 * slot + 1] = sc;
+  }
   // wave 0: candidate i = (wave i / k, round i % k), two per lane
   uint32_t ck[2], cid[2];
   float cv[2];
@@ -281,17 +309,16 @@ __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __
   // (the candidates' loads above are issued first: the two sets are
   // independent, so the wave waits for memory once)
   const float* ms = ws_ms + (size_t)row * C * 2;
-  // M = max m_c, then S = sum_c s_c e^(m_c - M) in chunk order (64 chunks at
-  // a time, each batch summed by the same fixed shuffle tree)
-  float M = -INFINITY;
-  for (int c = lane; c < C; c += 64) M = fmaxf(M, ms[2 * c]);
-  M = wave_max_f(M);
-  float S = 0.f;
+  // the row's (M, S) from the chunks' (m_c, s_c) by the pairwise rule, 64
+  // chunks at a time in a fixed order (chunks without mass, max -inf, add
+  // nothing; the row needs at least one finite logit)
+  float M = -INFINITY, S = 0.f;
   for (int c0 = 0; c0 < C; c0 += 64) {
     const int c = c0 + lane;
-    // chunks without mass (max -inf) add nothing; the row needs at least one
-    // finite logit (M finite)
-    S += wave_sum_f(c < C && ms[2 * c] != -INFINITY ? ms[2 * c + 1] * __expf(ms[2 * c] - M) : 0.f);
+    float mb = c < C ? ms[2 * c] : -INFINITY;
+    float sb = c < C && mb != -INFINITY ? ms[2 * c + 1] : 0.f;
+    wave_lse(mb, sb);
+    lse_add(M, S, mb, sb);
   }
   const float lse = M + __logf(S);
 
