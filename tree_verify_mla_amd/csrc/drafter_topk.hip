@@ -31,12 +31,14 @@ constexpr int CT = 256;            // threads per chunk workgroup
 constexpr int EPT = 32;            // logits per thread
 constexpr int CHUNK = CT * EPT;    // logits per chunk
 constexpr int KMAX = 32;           // largest k
+constexpr float LOG2E = 1.44269504088896340736f;
 constexpr int MERGE_PER_LANE = 16; // chunk candidates per lane in the merge (C * k <= 1024)
 
 // order-preserving map of a finite fp32 to uint32 (larger value -> larger key)
 __device__ inline uint32_t fkey(float f) {
-  const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);  // -0 ties with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.f);  // -0 + 0 = +0: -0 ties with +0
+  // negative: all bits flipped; otherwise the sign bit set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 // its inverse (key 0x80000000u gives +0)
 __device__ inline float funkey(uint32_t k) {
@@ -125,17 +127,16 @@ __device__ inline float to_f32(T x) {
   else return x;
 }
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits, int vocab, int C,
-                                                   int k, float* __restrict__ ws_ms,
-                                                   float* __restrict__ ws_val,
-                                                   int32_t* __restrict__ ws_id) {
-  __shared__ float red_m[CT / 64], red_s[CT / 64];
-  __shared__ uint2 cand[CT / 64][KMAX];   // each wave's k best: (key, id)
-  const int row = blockIdx.x / C, c = blockIdx.x % C;
+// Workgroup (row, c).  FULL: the chunk holds CHUNK logits (every chunk but
+// a row's last), so no element needs a bounds check.
+template <typename T, bool VEC, bool FULL>
+__device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int vocab, int C, int k,
+                                           float* __restrict__ ws_ms, float* __restrict__ ws_val,
+                                           int32_t* __restrict__ ws_id, int row, int c,
+                                           float* red_m, float* red_s, uint2 (*cand)[KMAX]) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const long long c0 = (long long)c * CHUNK;          // first element of the chunk in its row
-  const int n = (int)min((long long)CHUNK, vocab - c0);  // elements of the chunk
+  const int n = FULL ? CHUNK : (int)min((long long)CHUNK, vocab - c0);  // elements of the chunk
   const T* src = logits + (size_t)row * vocab + c0;
 
   float x[EPT];
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
 #pragma unroll
     for (int q = 0; q < EPT / W; ++q) {
       const int e = W * t + W * CT * q;
-      if (e + W <= n) {
+      if (FULL || e + W <= n) {
         const v16 raw = *reinterpret_cast<const v16*>(src + e);
         const T* vals = reinterpret_cast<const T*>(&raw);
 #pragma unroll
@@ -159,13 +160,13 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const int e = t + CT * j;
-      x[j] = e < n ? to_f32(src[e]) : -INFINITY;
+      x[j] = FULL || e < n ? to_f32(src[e]) : -INFINITY;
     }
   }
   uint32_t live = 0;  // bit j: register j holds an element of the chunk still in play
 #pragma unroll
   for (int j = 0; j < EPT; ++j)
-    if (elem_of<T, VEC>(t, j) < n) live |= 1u << j;
+    if (FULL || elem_of<T, VEC>(t, j) < n) live |= 1u << j;
 
   // The chunk's max m and sum s of e^(x - m): each lane's own (max, sum)
   // first, then the wave's and the workgroup's by the pairwise rule
@@ -176,11 +177,12 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) m = fmaxf(m, x[j]);
-  const float mref = m == -INFINITY ? 0.f : m;
+  // e^(x - m) as 2^(x log2 e - m log2 e): one fused multiply-add per element
+  const float mref = (m == -INFINITY ? 0.f : m) * LOG2E;
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < EPT; ++j)
-    if ((live >> j) & 1u) s += __expf(x[j] - mref);
+    if ((live >> j) & 1u) s += __builtin_amdgcn_exp2f(__fmaf_rn(x[j], LOG2E, -mref));
   wave_lse(m, s);
   if (lane == 0) {
     red_m[wave] = m;
@@ -277,6 +279,20 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
       if (second) ck[1] = 0u; else ck[0] = 0u;
     }
   }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits, int vocab, int C,
+                                                   int k, float* __restrict__ ws_ms,
+                                                   float* __restrict__ ws_val,
+                                                   int32_t* __restrict__ ws_id) {
+  __shared__ float red_m[CT / 64], red_s[CT / 64];
+  __shared__ uint2 cand[CT / 64][KMAX];  // each wave's k best: (key, id)
+  const int row = blockIdx.x / C, c = blockIdx.x % C;
+  if ((long long)(c + 1) * CHUNK <= vocab)
+    chunk_body<T, VEC, true>(logits, vocab, C, k, ws_ms, ws_val, ws_id, row, c, red_m, red_s, cand);
+  else
+    chunk_body<T, VEC, false>(logits, vocab, C, k, ws_ms, ws_val, ws_id, row, c, red_m, red_s, cand);
 }
 
 __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __restrict__ ws_ms,
