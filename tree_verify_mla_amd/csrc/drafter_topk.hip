@@ -86,6 +86,20 @@ __device__ inline uint32_t wave_ext(uint32_t x) {
   return op(op(r0, r1), op(r2, r3));
 }
 
+// Whether this lane holds the wave's best (key, id): the largest key, then
+// the smallest id among the lanes that hold it (ids are unique).  The id
+// reduction runs only when several lanes hold the largest key.  gk: the
+// wave's largest key.
+__device__ inline bool wave_owner(uint32_t key, uint32_t id, uint32_t& gk) {
+  gk = wave_ext<true>(key);
+  uint64_t hold = __ballot(key == gk);
+  if (__popcll(hold) > 1) {
+    const uint32_t gid = wave_ext<false>(key == gk ? id : 0xffffffffu);
+    hold = __ballot(key == gk && id == gid);
+  }
+  return (hold >> (threadIdx.x & 63)) & 1ull;
+}
+
 // (m, s) <- (m, s) + (m2, s2): a pair is a max and a sum of e^(x - max); a
 // max of -inf carries no mass
 __device__ inline void lse_add(float& m, float& s, float m2, float s2) {
@@ -226,12 +240,12 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
   best_two(0xffffffffu, -1, k1, j1, k2, j2);
   for (int r = 0; r < k; ++r) {
     const uint32_t myid = k1 ? (uint32_t)(c0 + elem_of_rt<T, VEC>(t, j1)) : 0xffffffffu;
-    const uint32_t wk = wave_ext<true>(k1);
-    const uint32_t wid = wave_ext<false>(k1 == wk ? myid : 0xffffffffu);
+    uint32_t wk;
+    const bool owner = wave_owner(k1, myid, wk);
     if (wk == 0u) {  // fewer than k logits in the wave
       if (lane == 0) cand[wave][r] = make_uint2(0u, 0xffffffffu);
-    } else if (k1 == wk && myid == wid) {  // the owner
-      cand[wave][r] = make_uint2(wk, wid);
+    } else if (owner) {
+      cand[wave][r] = make_uint2(wk, myid);
       if (k2 != 0u) {
         k1 = k2, j1 = j2, k2 = 0u;
       } else {
@@ -266,16 +280,16 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
     const bool second = ck[1] > ck[0] || (ck[1] == ck[0] && cid[1] < cid[0]);
     const uint32_t lk = second ? ck[1] : ck[0], lid = second ? cid[1] : cid[0];
     const float lv = second ? cv[1] : cv[0];
-    const uint32_t gk = wave_ext<true>(lk);
-    const uint32_t gid = wave_ext<false>(lk == gk ? lid : 0xffffffffu);
+    uint32_t gk;
+    const bool owner = wave_owner(lk, lid, gk);
     if (gk == 0u) {
       if (lane == 0) {
         ws_val[slot * k + r] = -INFINITY;
         ws_id[slot * k + r] = INT_MAX;
       }
-    } else if (lk == gk && lid == gid) {
+    } else if (owner) {
       ws_val[slot * k + r] = lv;
-      ws_id[slot * k + r] = (int32_t)gid;
+      ws_id[slot * k + r] = (int32_t)lid;
       if (second) ck[1] = 0u; else ck[0] = 0u;
     }
   }
@@ -361,11 +375,11 @@ __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __
     uint32_t hk = lane < C ? s_key[base] : 0u, hid = lane < C ? s_id[base] : 0xffffffffu;
     float hv = lane < C ? s_val[base] : 0.f;
     for (int r = 0; r < k; ++r) {
-      const uint32_t gk = wave_ext<true>(hk);
-      const uint32_t gid = wave_ext<false>(hk == gk ? hid : 0xffffffffu);
-      if (gk != 0u && hk == gk && hid == gid) {
+      uint32_t gk;
+      const bool owner = wave_owner(hk, hid, gk);
+      if (gk != 0u && owner) {
         out_val[(size_t)row * k + r] = hv - lse;
-        out_id[(size_t)row * k + r] = (int32_t)gid;
+        out_id[(size_t)row * k + r] = (int32_t)hid;
         ++pos;
         hk = pos < k ? s_key[base + pos] : 0u;
         hid = pos < k ? s_id[base + pos] : 0xffffffffu;
@@ -398,11 +412,11 @@ __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __
   float v1, v2;
   best_two(0xffffffffu, 0u, k1, i1, v1, k2, i2, v2);
   for (int r = 0; r < k; ++r) {
-    const uint32_t gk = wave_ext<true>(k1);
-    const uint32_t gid = wave_ext<false>(k1 == gk ? i1 : 0xffffffffu);
-    if (gk != 0u && k1 == gk && i1 == gid) {
+    uint32_t gk;
+    const bool owner = wave_owner(k1, i1, gk);
+    if (gk != 0u && owner) {
       out_val[(size_t)row * k + r] = v1 - lse;
-      out_id[(size_t)row * k + r] = (int32_t)gid;
+      out_id[(size_t)row * k + r] = (int32_t)i1;
       if (k2 != 0u) {
         k1 = k2, i1 = i2, v1 = v2, k2 = 0u;
       } else {
