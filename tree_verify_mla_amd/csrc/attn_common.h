@@ -9,8 +9,9 @@
 //    ranges of the global unit list (requests in order, tiles in order,
 //    blocks fastest).  A workgroup's range is a sequence of segments, each
 //    inside one tile; a segment that covers its whole tile writes the final
-//    output, any other writes a partial (unnormalised O, running max,
-//    running sum) into workspace slot 2*w + (first segment of w ? 0 : 1).
+//    output, any other writes a partial (O -- divided by the running sum in
+//    the matrix-core kernel --, running max, running sum) into workspace
+//    slot 2*w + (first segment of w ? 0 : 1).
 //    The ranges are equal in cost, not in units: every tile is preceded by
 //    KAPPA virtual units that stand for the cost of starting a segment
 //    (loading the rows' queries, filling the block pipeline, storing the
@@ -75,8 +76,11 @@ __device__ inline Params at_layer(Params p) {
   return p;
 }
 
-// floats per partial slot: O [mt][512], m [mt], l [mt]
+// floats per partial slot of the fp32 kernel: O [mt][512], m [mt], l [mt]
 __host__ __device__ constexpr long long slot_floats(int mt) { return (long long)mt * (DV + 2); }
+// the same for the matrix-core kernel, in float units: O / l [mt][512] in
+// fp16, then m [mt], l [mt] in fp32
+__host__ __device__ constexpr long long slot_floats_bf16(int mt) { return (long long)mt * (DV / 2 + 2); }
 
 struct Geom {
   int q0, Q, kv0, N, P, R, T, NB;

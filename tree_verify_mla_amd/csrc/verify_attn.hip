@@ -244,27 +244,30 @@ __device__ inline bool merge_plan_fast(const Params& p, int r, int t, const Geom
 }
 
 // Merge of the matrix-core kernel's split tiles.  That kernel stores a
-// partial in its accumulators' lane layout: wave w's store (rg, fb, gq)
-// writes 1 KB contiguously, lane l's 16 bytes holding features
-// 128 w + 32 fb + 8 gq + 4 (l >> 5) .. +3 of tile row 32 rg + (l & 31).
-// The 16 runs c = 4 fb + gq of one (tile, row group rg, feature quarter w)
-// are split into 16 / CPW parts of CPW runs; one single-wave workgroup per
-// part reads its runs (CPW loads of 1 KB per segment), so lane l folds the
-// segments for its own row with the same ordered log-sum-exp as
-// merge_kernel, the loads of LANES_BATCH segments issued before any is used.
-// The bf16 output goes through LDS and leaves as 16 CPW-byte row segments.
-// CPW = 4 spreads a small merge over twice as many compute units (each one
-// reads at a bounded rate); CPW = 8 keeps larger merges at fewer waves; the
-// smallest merges (fewer than 8 tiles) take CPW = 2 with 8 segments' loads
-// in flight.
+// partial as O / l in fp16 in its accumulators' lane layout -- wave w's
+// store (rg, fb, gp) writes 1 KB contiguously, lane l's 16 bytes holding
+// features 128 w + 32 fb + 16 gp + 4 (l >> 5) .. +3 and the same + 8 of tile
+// row 32 rg + (l & 31) -- and then m and l of every row in fp32.  So the 8
+// runs c = 2 fb + gp of one (tile, row group rg, feature quarter w) hold
+// features 16 c .. 16 c + 15 of the quarter; they are split into 8 / CPW
+// parts of CPW runs, and one single-wave workgroup per part reads its runs
+// (CPW loads of 1 KB per segment), so that lane l folds the segments for
+// its own row with the same ordered log-sum-exp as merge_kernel, the loads
+// of LANES_BATCH segments issued before any is used: segment j enters with
+// the weight l_j 2^(m_j - M).  The bf16 output goes through LDS and leaves
+// as 32 CPW-byte row segments.  CPW = 2 spreads a small merge over twice as
+// many compute units (each one reads at a bounded rate); CPW = 4 keeps
+// larger merges at fewer waves; the smallest merges (fewer than 8 tiles)
+// take CPW = 1 with 8 segments' loads in flight.
 template <int CPW, int LANES_BATCH>
 __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p_all, int G) {
-  static_assert(CPW == 2 || CPW == 4 || CPW == 8, "runs per wave");
+  static_assert(CPW == 1 || CPW == 2 || CPW == 4, "runs per wave");
   const Params p = at_layer(p_all);
-  constexpr int mt = MT_BF16, RG = 4, FB = 4, NH = 16 / CPW;
-  constexpr int STR = 16 * CPW + 16;  // bytes per staged row (padded)
+  constexpr int mt = MT_BF16, RG = 4, NH = 8 / CPW;
+  constexpr int STR = 32 * CPW + 16;  // bytes per staged row (padded)
   typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
   __shared__ __align__(16) char stg[32 * STR];
   const int q = blockIdx.x % (16 * NH), tile = blockIdx.x / (16 * NH);
   const int h = q % NH, rg = (q / NH) >> 2, w = (q / NH) & 3;
@@ -277,24 +280,25 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p_all, int G) {
   if (t * mt + 32 * rg >= g.R) return;  // a row group without live rows (its partials are not stored)
   const int lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
   const int row = 32 * rg + l32;  // tile row of this lane
-  const long long sf = slot_floats(mt);
-  const long long run = ((long long)(w * RG + rg) * FB * 4 + CPW * h) * 256 + 4 * lane;
+  const long long sf = slot_floats_bf16(mt);
+  const long long run = ((long long)(w * RG + rg) * 8 + CPW * h) * 512 + 8 * lane;  // in halves
 
   float M = -INFINITY, L = 0.f;
-  float acc[4 * CPW];
+  float acc[8 * CPW];
 #pragma unroll
-  for (int e = 0; e < 4 * CPW; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 8 * CPW; ++e) acc[e] = 0.f;
   for (long long k0 = 0; k0 < m.nseg; k0 += LANES_BATCH) {
     float ms[LANES_BATCH], ls[LANES_BATCH];
-    float4 x[LANES_BATCH][CPW];
+    f16x8 x[LANES_BATCH][CPW];
 #pragma unroll
     for (int j = 0; j < LANES_BATCH; ++j) {
       if (k0 + j < m.nseg) {
         const float* base =
             p.ws + merge_slot(p, k0 + j, m.first_slot, m.w_first, m.vtile, m.V, m.Ge) * sf;
-        ms[j] = base[(long long)mt * DV + row];
-        ls[j] = base[(long long)mt * DV + mt + row];
-        const float4* src = reinterpret_cast<const float4*>(base + run);
+        const float* stats = base + (long long)mt * DV / 2;
+        ms[j] = stats[row];
+        ls[j] = stats[mt + row];
+        const f16x8* src = reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(base) + run);
 #pragma unroll
         for (int c = 0; c < CPW; ++c) x[j][c] = src[c * 64];
       }
@@ -304,37 +308,38 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p_all, int G) {
       if (k0 + j >= m.nseg || ms[j] == -INFINITY) continue;  // a segment that saw no column
       const float Mn = fmaxf(M, ms[j]);
       const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
-      const float b = exp2f(ms[j] - Mn);
+      const float wj = ls[j] * exp2f(ms[j] - Mn);
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) {
-        acc[4 * c] = acc[4 * c] * a + x[j][c].x * b;
-        acc[4 * c + 1] = acc[4 * c + 1] * a + x[j][c].y * b;
-        acc[4 * c + 2] = acc[4 * c + 2] * a + x[j][c].z * b;
-        acc[4 * c + 3] = acc[4 * c + 3] * a + x[j][c].w * b;
-      }
-      L = L * a + ls[j] * b;
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[8 * c + e] = acc[8 * c + e] * a + (float)x[j][c][e] * wj;
+      L = L * a + wj;
       M = Mn;
     }
   }
   const float inv = 1.f / L;
-  // run CPW h + c holds features 8 (CPW h + c) + 4 hl .. +3 of the quarter
+  // run CPW h + c holds features 16 (CPW h + c) + 4 hl .. +3 and + 8 of the
+  // quarter
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    bf16x4 v;
+  for (int c = 0; c < CPW; ++c)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * c + e] * inv);
-    *reinterpret_cast<bf16x4*>(stg + l32 * STR + 2 * (8 * c + 4 * hl)) = v;
-  }
+    for (int half = 0; half < 2; ++half) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[8 * c + 4 * half + e] * inv);
+      *reinterpret_cast<bf16x4*>(stg + l32 * STR + 2 * (16 * c + 8 * half + 4 * hl)) = v;
+    }
   __syncthreads();
   const size_t row0 = (size_t)g.q0 * p.H + (size_t)t * mt + 32 * rg;  // output row of tile row 32 rg
-  constexpr int RPI = 64 / CPW;  // rows per instruction (CPW lanes of 16 bytes per row)
+  constexpr int LPR = 2 * CPW;   // lanes of 16 bytes per staged row
+  constexpr int RPI = 64 / LPR;  // rows per instruction
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
-    const int tr = RPI * i + lane / CPW, col = lane % CPW;
+    const int tr = RPI * i + lane / LPR, col = lane % LPR;
     const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + tr * STR + 16 * col);
     if (t * mt + 32 * rg + tr < g.R)
       *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + (row0 + tr) * DV + 128 * w +
-                                 8 * CPW * h + 8 * col) = v;
+                                 16 * CPW * h + 8 * col) = v;
   }
   if (p.lse && w == 0 && h == 0 && hl == 0 && t * mt + row < g.R)
     p.lse[row0 + l32] = (M + log2f(L)) * LN2;
@@ -349,19 +354,19 @@ int launch_f32(const Params& p, int grid, hipStream_t s) {
 
 int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s) {
   if (mt == MT_BF16) {  // the matrix-core kernel's lane-layout partials (bf16 output)
-    // fewer than four waves per compute unit at 8 runs per wave: 4 runs; at
-    // 4 runs: 2
+    // fewer than four waves per compute unit at 4 runs per wave: 2 runs; at
+    // 2 runs: 1
     const long long tiles = (long long)p.bs * p.T_max * p.L;
     const long long cus = device_cu_count();
     if (tiles * 128 < 4LL * cus) {
-      hipLaunchKernelGGL((merge_lanes_kernel<2, 8>), dim3((unsigned)(p.bs * p.T_max * 128), p.L),
+      hipLaunchKernelGGL((merge_lanes_kernel<1, 8>), dim3((unsigned)(p.bs * p.T_max * 128), p.L),
                          dim3(64), 0, s, p, grid_groups);
     } else if (tiles * 32 < 4LL * cus) {
-      hipLaunchKernelGGL((merge_lanes_kernel<4, 4>), dim3((unsigned)(p.bs * p.T_max * 64), p.L), dim3(64),
-                         0, s, p, grid_groups);
+      hipLaunchKernelGGL((merge_lanes_kernel<2, 4>), dim3((unsigned)(p.bs * p.T_max * 64), p.L),
+                         dim3(64), 0, s, p, grid_groups);
     } else {
-      hipLaunchKernelGGL((merge_lanes_kernel<8, 4>), dim3((unsigned)(p.bs * p.T_max * 32), p.L), dim3(64),
-                         0, s, p, grid_groups);
+      hipLaunchKernelGGL((merge_lanes_kernel<4, 4>), dim3((unsigned)(p.bs * p.T_max * 32), p.L),
+                         dim3(64), 0, s, p, grid_groups);
     }
     return check_launch("verify_attn(merge)");
   }
@@ -391,7 +396,8 @@ extern "C" size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int m
   } else if (num_splits > 1) {
     slots = (long long)bs * T_max * num_splits;
   }
-  return (size_t)(slots * slot_floats(mt) * (long long)sizeof(float));
+  const long long sf = dtype == DDTREE_BF16 ? slot_floats_bf16(mt) : slot_floats(mt);
+  return (size_t)(slots * sf * (long long)sizeof(float));
 }
 
 namespace {

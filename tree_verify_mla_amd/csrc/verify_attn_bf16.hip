@@ -71,6 +71,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef short __attribute__((ext_vector_type(4))) i16x4_t;
 typedef uint32_t __attribute__((ext_vector_type(4))) u32x4_t;
@@ -858,30 +859,38 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
       continue;
     }
     {
-      // fp32 partial in the accumulator's lane layout: store (rg, fb, gq) of
-      // wave w writes 1 KB contiguously, lane l's 16 bytes (features
-      // 128 w + 32 fb + 8 gq + 4 (l >> 5) .. +3 of tile row 32 rg + (l & 31))
-      // at float offset (((w RG + rg) FB + fb) 4 + gq) 256 + 4 l.
-      // Row groups without a live row are not stored (nothing reads them).
-      float* base = p.ws + slot * slot_floats(MT);
-      float* ob = base + (size_t)wave * (RG * FB * 4 * 256) + 4 * lane;
+      // The partial, normalised: O / l of every row, a weighted mean of the
+      // c_kv rows it saw (so no larger than their largest element), in fp16,
+      // then the rows' m and l in fp32.  Lane layout of the accumulator:
+      // store (rg, fb, gp) of wave w writes 1 KB contiguously, lane l's 16
+      // bytes holding features 128 w + 32 fb + 16 gp + 4 (l >> 5) .. +3 and
+      // the same + 8 of tile row 32 rg + (l & 31), at half offset
+      // (((w RG + rg) FB + fb) 2 + gp) 512 + 8 l.  Row groups without a live
+      // row are not stored (nothing reads them); a row that saw no column
+      // (l = 0, m = -inf) stores zeros, and the merge skips it.
+      float* base = p.ws + slot * slot_floats_bf16(MT);
+      _Float16* ob = reinterpret_cast<_Float16*>(base) + (size_t)wave * (RG * FB * 2 * 512) + 8 * lane;
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
         if (t * MT + 32 * rg >= g.R) continue;
+        const float inv = lrow[rg] > 0.f ? 1.f / lrow[rg] : 0.f;
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
+          for (int gp = 0; gp < 2; ++gp) {
             const f32x16_t& x = o[rg][fb];
-            const f32x4_t v4 = {x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]};
-            *reinterpret_cast<f32x4_t*>(ob + ((rg * FB + fb) * 4 + gq) * 256) = v4;
+            f16x8_t v8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v8[e] = (_Float16)(x[8 * gp + e] * inv);
+            *reinterpret_cast<f16x8_t*>(ob + ((rg * FB + fb) * 2 + gp) * 512) = v8;
           }
       }
       if (wave == 0 && hl == 0) {
+        float* stats = base + (size_t)MT * DV / 2;
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-          base[(size_t)MT * DV + 32 * rg + l32] = mrow[rg];
-          base[(size_t)MT * DV + MT + 32 * rg + l32] = lrow[rg];
+          stats[32 * rg + l32] = mrow[rg];
+          stats[MT + 32 * rg + l32] = lrow[rg];
         }
       }
     }
