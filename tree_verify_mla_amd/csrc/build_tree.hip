@@ -191,11 +191,13 @@ __device__ inline uint32_t lane_val(uint32_t x, int src_lane) {
 template <bool MAX>
 __device__ inline uint32_t wave_ext(uint32_t x) {
   auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  // the operation's identity as the DPP fill value lets the move fold into it
+  constexpr int ID = MAX ? 0 : -1;
   // inside each 16-lane row: swap neighbours, pairs, then mirror halves
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)x, 0xB1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)x, 0x4E, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)x, 0x141, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)x, 0x140, 0xF, 0xF, false));
   return op(op(lane_val(x, 0), lane_val(x, 16)), op(lane_val(x, 32), lane_val(x, 48)));
 }
 

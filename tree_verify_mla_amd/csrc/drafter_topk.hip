@@ -75,10 +75,12 @@ __device__ inline int elem_of_rt(int t, int j) {
 template <bool MAX>
 __device__ inline uint32_t wave_ext(uint32_t x) {
   auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));
+  // the operation's identity as the DPP fill value lets the move fold into it
+  constexpr int ID = MAX ? 0 : -1;
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)x, 0xB1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)x, 0x4E, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)x, 0x141, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)x, 0x140, 0xF, 0xF, false));
   const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
   const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
   const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
