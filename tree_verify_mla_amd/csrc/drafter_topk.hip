@@ -220,7 +220,7 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
   // 2. after one barrier, wave 0 takes the chunk's k best out of the 4 k
   //    wave candidates in LDS the same way.
   // The keys take the logits' place (a key gives its logit back), which
-  // keeps the kernel within the registers of five waves per SIMD.
+  // keeps the kernel within the registers of six waves per SIMD.
   uint32_t key[EPT];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) key[j] = ((live >> j) & 1u) ? fkey(x[j]) : 0u;
@@ -229,7 +229,9 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
     k1 = 0u, j1 = 0, k2 = 0u, j2 = 0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-      const uint32_t kj = (key[j] < lk || (key[j] == lk && j > lj)) ? key[j] : 0u;
+      // bitwise, not short-circuit: no branches around the comparisons
+      const bool after = (key[j] < lk) | ((key[j] == lk) & (j > lj));
+      const uint32_t kj = after ? key[j] : 0u;
       const bool first = kj > k1, second = !first && kj > k2;
       k2 = first ? k1 : (second ? kj : k2);
       j2 = first ? j1 : (second ? j : j2);
