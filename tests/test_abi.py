@@ -104,8 +104,9 @@ def test_workspace_size_forced_split(lib):
     assert lib.ddtree_verify_attn_workspace_size(2, 8, 33, 100, 1, _lib.DDTREE_F32) == 0
     assert lib.ddtree_verify_attn_workspace_size(2, 8, 33, 100, 0, _lib.DDTREE_F32) == 0
     # bf16 tiles hold 128 rows -> 3 tiles
-    # bf16: per slot O / l of 128 rows x 512 in fp16, then m and l in fp32
-    assert lib.ddtree_verify_attn_workspace_size(1, 8, 33, 100, 2, _lib.DDTREE_BF16) == 3 * 2 * 128 * (256 + 2) * 4
+    # bf16: per slot O / l of 128 rows x 512 in fp16, then m, l and four
+    # quarter scales per row in fp32
+    assert lib.ddtree_verify_attn_workspace_size(1, 8, 33, 100, 2, _lib.DDTREE_BF16) == 3 * 2 * 128 * (256 + 6) * 4
     assert lib.ddtree_verify_attn_workspace_size(-1, 8, 33, 100, 2, _lib.DDTREE_BF16) == 0
 
 

@@ -127,6 +127,29 @@ def test_c2_shard_bf16_full_compare(num_splits):
     _check_attention(orc, st)
 
 
+@pytest.mark.parametrize("shift", [20, -40])
+def test_partials_any_magnitude(shift):
+    """c_kv scaled by 2^shift and the queries' c_kv part by 2^-shift: the
+    scores are unchanged (powers of two are exact in bf16) and every output
+    scales by 2^shift.  2^20 puts |c_kv| far above the largest fp16 (65504)
+    and 2^-40 far below its smallest normal, so the split tiles' fp16
+    partials must carry their per-row scale to match the oracle."""
+    _say(f"test_partials_any_magnitude shift={shift}")
+    import copy
+    from workloads.gen import bf16_bits_to_f32, f32_to_bf16_bits
+    wl = copy.copy(make_workload(get_config(2)))
+    pool = bf16_bits_to_f32(wl.kv_pool)
+    q = bf16_bits_to_f32(wl.q)
+    pool[:, :512] *= np.float32(2.0 ** shift)
+    q[:, :, :512] *= np.float32(2.0 ** -shift)
+    wl.kv_pool = f32_to_bf16_bits(pool)
+    wl.q = f32_to_bf16_bits(q)
+    assert np.array_equal(bf16_bits_to_f32(wl.kv_pool)[:, :512], pool[:, :512], equal_nan=True)  # exact (unused rows hold NaN)
+    for num_splits in (0, 7):
+        orc, st = _run(wl, num_splits)
+        _check_attention(orc, st)
+
+
 def test_ragged_edges_bf16():
     """Empty and odd prefixes, budget 0 (autoregressive), ragged tails across tiles."""
     _say("test_ragged_edges_bf16")

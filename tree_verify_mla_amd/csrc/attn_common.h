@@ -79,8 +79,9 @@ __device__ inline Params at_layer(Params p) {
 // floats per partial slot of the fp32 kernel: O [mt][512], m [mt], l [mt]
 __host__ __device__ constexpr long long slot_floats(int mt) { return (long long)mt * (DV + 2); }
 // the same for the matrix-core kernel, in float units: O / l [mt][512] in
-// fp16, then m [mt], l [mt] in fp32
-__host__ __device__ constexpr long long slot_floats_bf16(int mt) { return (long long)mt * (DV / 2 + 2); }
+// fp16 (scaled per row and 128-feature quarter), then m [mt], l [mt] and the
+// inverse scales [4][mt] in fp32
+__host__ __device__ constexpr long long slot_floats_bf16(int mt) { return (long long)mt * (DV / 2 + 2 + 4); }
 
 struct Geom {
   int q0, Q, kv0, N, P, R, T, NB;

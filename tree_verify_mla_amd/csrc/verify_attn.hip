@@ -244,7 +244,9 @@ __device__ inline bool merge_plan_fast(const Params& p, int r, int t, const Geom
 }
 
 // Merge of the matrix-core kernel's split tiles.  That kernel stores a
-// partial as O / l in fp16 in its accumulators' lane layout -- wave w's
+// partial as O / l in fp16 (times a power-of-two scale per row and feature
+// quarter, whose inverse it stores too) in its accumulators' lane layout --
+// wave w's
 // store (rg, fb, gp) writes 1 KB contiguously, lane l's 16 bytes holding
 // features 128 w + 32 fb + 16 gp + 4 (l >> 5) .. +3 and the same + 8 of tile
 // row 32 rg + (l & 31) -- and then m and l of every row in fp32.  So the 8
@@ -254,7 +256,7 @@ __device__ inline bool merge_plan_fast(const Params& p, int r, int t, const Geom
 // (CPW loads of 1 KB per segment), so that lane l folds the segments for
 // its own row with the same ordered log-sum-exp as merge_kernel, the loads
 // of LANES_BATCH segments issued before any is used: segment j enters with
-// the weight l_j 2^(m_j - M).  The bf16 output goes through LDS and leaves
+// the weight l_j 2^(m_j - M) (its values times their inverse scale).  The bf16 output goes through LDS and leaves
 // as 32 CPW-byte row segments.  CPW = 2 spreads a small merge over twice as
 // many compute units (each one reads at a bounded rate); CPW = 4 keeps
 // larger merges at fewer waves; the smallest merges (fewer than 8 tiles)
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p_all, int G) {
 #pragma unroll
   for (int e = 0; e < 8 * CPW; ++e) acc[e] = 0.f;
   for (long long k0 = 0; k0 < m.nseg; k0 += LANES_BATCH) {
-    float ms[LANES_BATCH], ls[LANES_BATCH];
+    float ms[LANES_BATCH], ls[LANES_BATCH], us[LANES_BATCH];
     f16x8 x[LANES_BATCH][CPW];
 #pragma unroll
     for (int j = 0; j < LANES_BATCH; ++j) {
@@ -298,6 +300,7 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p_all, int G) {
         const float* stats = base + (long long)mt * DV / 2;
         ms[j] = stats[row];
         ls[j] = stats[mt + row];
+        us[j] = stats[(2 + w) * mt + row];
         const f16x8* src = reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(base) + run);
 #pragma unroll
         for (int c = 0; c < CPW; ++c) x[j][c] = src[c * 64];
@@ -309,10 +312,11 @@ __global__ __launch_bounds__(64) void merge_lanes_kernel(Params p_all, int G) {
       const float Mn = fmaxf(M, ms[j]);
       const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
       const float wj = ls[j] * exp2f(ms[j] - Mn);
+      const float wv = wj * us[j];  // the stored values carry the quarter's scale
 #pragma unroll
       for (int c = 0; c < CPW; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[8 * c + e] = acc[8 * c + e] * a + (float)x[j][c][e] * wj;
+        for (int e = 0; e < 8; ++e) acc[8 * c + e] = acc[8 * c + e] * a + (float)x[j][c][e] * wv;
       L = L * a + wj;
       M = Mn;
     }

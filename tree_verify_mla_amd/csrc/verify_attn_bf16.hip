@@ -860,20 +860,34 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
     }
     {
       // The partial, normalised: O / l of every row, a weighted mean of the
-      // c_kv rows it saw (so no larger than their largest element), in fp16,
-      // then the rows' m and l in fp32.  Lane layout of the accumulator:
-      // store (rg, fb, gp) of wave w writes 1 KB contiguously, lane l's 16
-      // bytes holding features 128 w + 32 fb + 16 gp + 4 (l >> 5) .. +3 and
-      // the same + 8 of tile row 32 rg + (l & 31), at half offset
-      // (((w RG + rg) FB + fb) 2 + gp) 512 + 8 l.  Row groups without a live
-      // row are not stored (nothing reads them); a row that saw no column
-      // (l = 0, m = -inf) stores zeros, and the merge skips it.
+      // c_kv rows it saw, in fp16 after a power-of-two scale per row and
+      // feature quarter that brings its largest magnitude into [2^14, 2^15)
+      // (any finite c_kv fits, and small rows keep fp16's full precision),
+      // then the rows' m and l and the four quarters' inverse scales in fp32.
+      // Lane layout of the accumulator: store (rg, fb, gp) of wave w writes
+      // 1 KB contiguously, lane l's 16 bytes holding features 128 w + 32 fb +
+      // 16 gp + 4 (l >> 5) .. +3 and the same + 8 of tile row 32 rg +
+      // (l & 31), at half offset (((w RG + rg) FB + fb) 2 + gp) 512 + 8 l.
+      // Row groups without a live row are not stored (nothing reads them); a
+      // row that saw no column (l = 0, m = -inf) stores zeros, and the merge
+      // skips it.
       float* base = p.ws + slot * slot_floats_bf16(MT);
+      float* stats = base + (size_t)MT * DV / 2;  // m [MT], l [MT], 1 / scale [4][MT]
       _Float16* ob = reinterpret_cast<_Float16*>(base) + (size_t)wave * (RG * FB * 2 * 512) + 8 * lane;
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
         if (t * MT + 32 * rg >= g.R) continue;
         const float inv = lrow[rg] > 0.f ? 1.f / lrow[rg] : 0.f;
+        float mx = 0.f;  // the row's largest |O| in this quarter (lanes l and l ^ 32)
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(o[rg][fb][e]));
+        mx = fmaxf(mx, other_half(mx)) * inv;
+        int ex = 0;
+        (void)frexpf(mx, &ex);  // mx < 2^ex (ex = 0 for mx = 0)
+        ex = min(max(ex, -100), 100);
+        const float f = inv * ldexpf(1.f, 15 - ex);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -881,12 +895,12 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
             const f32x16_t& x = o[rg][fb];
             f16x8_t v8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v8[e] = (_Float16)(x[8 * gp + e] * inv);
+            for (int e = 0; e < 8; ++e) v8[e] = (_Float16)(x[8 * gp + e] * f);
             *reinterpret_cast<f16x8_t*>(ob + ((rg * FB + fb) * 2 + gp) * 512) = v8;
           }
+        if (hl == 0) stats[2 * MT + wave * MT + 32 * rg + l32] = ldexpf(1.f, ex - 15);
       }
       if (wave == 0 && hl == 0) {
-        float* stats = base + (size_t)MT * DV / 2;
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
           stats[32 * rg + l32] = mrow[rg];
