@@ -213,7 +213,9 @@ size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int max_q_len, i
  *              bytes (may be NULL when that is 0).
  * Arithmetic: bf16 inputs use bf16 matrix cores with fp32 accumulation, the
  * softmax weights rounded to bf16 for the value product, output rounded to
- * bf16; f32 inputs compute in fp32 throughout, on a vector-ALU kernel meant
+ * bf16; a split tile's partial results pass to the merge as O / l in fp16
+ * (scaled per row and 128 features by a power of two into fp16's range, so
+ * any finite c_kv is handled) with m and l in fp32; f32 inputs compute in fp32 throughout, on a vector-ALU kernel meant
  * for small batches and for checking the bf16 path: each of its query rows
  * reads its request's KV rows itself, so its time grows as H * Q * N (any
  * size is accepted and correct).
