@@ -150,6 +150,19 @@ def test_partials_any_magnitude(shift):
         _check_attention(orc, st)
 
 
+def test_one_tile_over_the_whole_device_bf16():
+    """A single 34-row tile over a 60,000-column prefix: the persistent
+    schedule splits it over about 220 workgroups and the merge folds that
+    many segments of one tile; a second request (one 2-row tile, no tree
+    nodes) takes the remaining workgroups."""
+    _say("test_one_tile_over_the_whole_device_bf16")
+    wl = make_workload(get_config(3), bs=2, heads=2, budgets=[16, 0], prefixes=[60000, 9000],
+                       pool_slots=80000, seed=4242)
+    orc, st = _run(wl)
+    _check_integer_stages(orc, st)
+    _check_attention(orc, st)
+
+
 def test_ragged_edges_bf16():
     """Empty and odd prefixes, budget 0 (autoregressive), ragged tails across tiles."""
     _say("test_ragged_edges_bf16")
