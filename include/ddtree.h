@@ -206,9 +206,13 @@ size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int max_q_len, i
  *              scaled scores.
  *   num_splits 0 = automatic (bf16: persistent work split evenly over the
  *              device's compute units, partial results merged by log-sum-exp;
- *              f32: no split); S >= 1 = each row tile's KV range cut into S
- *              equal parts, then merged.  The result does not depend on the
- *              split beyond rounding.
+ *              bf16 calls too small to fill the device that way -- at most
+ *              4 units of 128 rows x 32 KV columns per compute unit by the
+ *              host bounds -- take 32-row tiles with each tile's KV range cut
+ *              into a fixed number of parts, see ddtree_verify_attn_plan;
+ *              f32: no split); S >= 1 = each 128-row tile's KV range cut
+ *              into S equal parts, then merged.  The result does not depend
+ *              on the split beyond rounding.
  *   workspace  device scratch of at least ddtree_verify_attn_workspace_size()
  *              bytes (may be NULL when that is 0).
  * Arithmetic: bf16 inputs use bf16 matrix cores with fp32 accumulation, the
@@ -231,6 +235,21 @@ int ddtree_verify_attn(const void* q, const void* kv_pool, int64_t num_slots,
                        int bs, int num_heads, int max_q_len, int max_kv_len, float scale,
                        int dtype, void* out, float* lse, int num_splits, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * ddtree_verify_attn_plan -- the kernel and split that ddtree_verify_attn
+ * (and, per layer, ddtree_verify_attn_layers) uses for these host bounds on
+ * the current device, for tests and measurement.
+ *   tile_rows  out: query rows per tile -- 128 (bf16 matrix-core kernel,
+ *              persistent schedule or forced splits), 32 (bf16 kernel for
+ *              calls too small to fill the device; see num_splits above) or
+ *              4 (f32 kernel).
+ *   splits     out: KV parts per tile; 0 for the persistent schedule.
+ * Errors: EINVAL (null output, sizes or dtype invalid as for
+ * ddtree_verify_attn); EHIP (the device's compute units cannot be read).
+ */
+int ddtree_verify_attn_plan(int bs, int num_heads, int max_q_len, int max_kv_len,
+                            int num_splits, int dtype, int* tile_rows, int* splits);
 
 /*
  * ddtree_verify_attn_layers -- ddtree_verify_attn over L layers in one

@@ -110,6 +110,21 @@ def test_workspace_size_forced_split(lib):
     assert lib.ddtree_verify_attn_workspace_size(-1, 8, 33, 100, 2, _lib.DDTREE_BF16) == 0
 
 
+def test_verify_attn_plan_validation(lib):
+    rows, splits = ctypes.c_int(-7), ctypes.c_int(-7)
+    out = (ctypes.byref(rows), ctypes.byref(splits))
+    assert lib.ddtree_verify_attn_plan(1, 8, 33, 4129, 0, _lib.DDTREE_BF16, NULL, out[1]) == EINVAL
+    assert lib.ddtree_verify_attn_plan(1, 0, 33, 4129, 0, _lib.DDTREE_BF16, *out) == EINVAL
+    assert lib.ddtree_verify_attn_plan(1, 8, 33, 32, 0, _lib.DDTREE_BF16, *out) == EINVAL
+    assert lib.ddtree_verify_attn_plan(1, 8, 33, 4129, -1, _lib.DDTREE_BF16, *out) == EINVAL
+    assert lib.ddtree_verify_attn_plan(1, 8, 33, 4129, 0, 7, *out) == EINVAL
+    # the fp32 kernel needs no device to plan: 4-row tiles, one part unless forced
+    assert lib.ddtree_verify_attn_plan(1, 8, 33, 4129, 0, _lib.DDTREE_F32, *out) == 0
+    assert (rows.value, splits.value) == (4, 1)
+    assert lib.ddtree_verify_attn_plan(1, 8, 33, 4129, 3, _lib.DDTREE_F32, *out) == 0
+    assert (rows.value, splits.value) == (4, 3)
+
+
 def test_accept_validation(lib):
     f = lib.ddtree_accept
     assert f(FAKE, FAKE, FAKE, FAKE, -1, 7, FAKE, FAKE, FAKE, FAKE, NULL) == EINVAL

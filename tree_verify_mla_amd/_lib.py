@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     lib.ddtree_compile_visibility.argtypes = [P, P, P, P, I, I, I, P, P, P, P, P]
     lib.ddtree_verify_attn_workspace_size.restype = SZ
     lib.ddtree_verify_attn_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.ddtree_verify_attn_plan.restype = I
+    lib.ddtree_verify_attn_plan.argtypes = [I, I, I, I, I, I, P, P]
     lib.ddtree_verify_attn.restype = I
     lib.ddtree_verify_attn.argtypes = [P, P, I64, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P, SZ, P]
     lib.ddtree_verify_attn_layers_workspace_size.restype = SZ
@@ -150,6 +152,16 @@ def ddtree_compile_visibility(node_parents, node_depths, qo_indptr, prefix_lens,
         bs, int(max_q_len), W, _p(vis_bits, torch.int32, "vis_bits"),
         _p(positions, torch.int64, "positions"), _p(dense_mask, torch.uint8, "dense_mask"),
         _p(mask_indptr, torch.int64, "mask_indptr"), _stream(stream)))
+
+
+def ddtree_verify_attn_plan(bs: int, num_heads: int, max_q_len: int, max_kv_len: int,
+                            num_splits: int, dtype: int) -> tuple:
+    """(tile_rows, splits) of the verify-attention kernel these bounds select."""
+    rows, splits = ctypes.c_int(0), ctypes.c_int(0)
+    _check("ddtree_verify_attn_plan",
+           load().ddtree_verify_attn_plan(bs, num_heads, max_q_len, max_kv_len, num_splits, dtype,
+                                          ctypes.byref(rows), ctypes.byref(splits)))
+    return rows.value, splits.value
 
 
 def ddtree_verify_attn_workspace_size(bs: int, num_heads: int, max_q_len: int, max_kv_len: int,

@@ -41,6 +41,13 @@ constexpr int MIN_UNITS = 8;    // smallest persistent range per workgroup
 constexpr int KAPPA = 8;        // virtual units ahead of every tile (cost of a segment start)
 constexpr int MT_BF16 = 128;    // rows per tile, bf16 matrix-core kernel (4 waves x 32 rows)
 constexpr int MT_F32 = 4;       // rows per tile, fp32 kernel
+constexpr int MT_NARROW = 32;   // rows per tile, bf16 kernel for small problems
+// The small-problem kernel serves single-layer bf16 calls whose 128-row work
+// units (tile x KV block, host bounds) number at most NARROW_UNITS_PER_CU per
+// compute unit.  Its split count S gives every workgroup the fewest steps of
+// NARROW_STEP blocks that at most one workgroup per compute unit allows.
+constexpr int NARROW_UNITS_PER_CU = 4;
+constexpr int NARROW_STEP = 4;
 
 struct Params {
   const void* q;
@@ -82,6 +89,34 @@ __host__ __device__ constexpr long long slot_floats(int mt) { return (long long)
 // fp16 (scaled per row and 128-feature quarter), then m [mt], l [mt] and the
 // inverse scales [4][mt] in fp32
 __host__ __device__ constexpr long long slot_floats_bf16(int mt) { return (long long)mt * (DV / 2 + 2 + 4); }
+
+// floats per partial slot of the small-problem kernel: O / l [32][512] in
+// fp16 (scaled per row and 128-feature quarter), m [32], l [32], inverse
+// scales [4][32]
+__host__ __device__ constexpr long long slot_floats_narrow() { return (long long)MT_NARROW * (DV / 2 + 2 + 4); }
+
+// Split plan of the small-problem kernel from the host bounds; false when
+// the call takes the 128-row kernel.  G = compute units.
+struct NarrowPlan {
+  int T;  // 32-row tiles per request (upper bound)
+  int S;  // ranges per tile
+};
+inline bool narrow_plan(int bs, int H, int max_q_len, int max_kv_len, int G, NarrowPlan& np) {
+  if (G <= 0) return false;
+  const long long nb = ((long long)max_kv_len + KB - 1) / KB;
+  const long long t128 = ((long long)max_q_len * H + MT_BF16 - 1) / MT_BF16;
+  if ((long long)bs * t128 * nb > (long long)NARROW_UNITS_PER_CU * G) return false;
+  const long long t32 = ((long long)max_q_len * H + MT_NARROW - 1) / MT_NARROW;
+  const long long tiles = (long long)bs * t32;
+  long long cap = G / tiles;  // ranges per tile that keep one workgroup per compute unit
+  if (cap < 1) cap = 1;
+  const long long steps = (nb + NARROW_STEP * cap - 1) / (NARROW_STEP * cap);
+  long long S = (nb + NARROW_STEP * steps - 1) / (NARROW_STEP * steps);
+  if (S < 1) S = 1;
+  np.T = (int)t32;
+  np.S = (int)S;
+  return true;
+}
 
 struct Geom {
   int q0, Q, kv0, N, P, R, T, NB;
@@ -226,5 +261,8 @@ namespace attn {
 int launch_f32(const Params& p, int grid, hipStream_t s);
 int launch_bf16(const Params& p, int grid, hipStream_t s);
 int launch_merge(const Params& p, int mt, int grid_groups, int dtype, hipStream_t s);
+// the small-problem kernel and, for S > 1, its merge (p.T_max = 32-row
+// tiles, p.S = ranges per tile)
+int launch_narrow(const Params& p, hipStream_t s);
 }  // namespace attn
 }  // namespace ddtree

@@ -392,6 +392,11 @@ extern "C" size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int m
   if (bs <= 0 || num_heads < 1 || max_q_len < 1 || max_kv_len < max_q_len || num_splits < 0)
     return 0;
   if (dtype != DDTREE_F32 && dtype != DDTREE_BF16) return 0;
+  NarrowPlan np;
+  if (dtype == DDTREE_BF16 && num_splits == 0 &&
+      narrow_plan(bs, num_heads, max_q_len, max_kv_len, bf16_grid(), np))
+    return np.S == 1 ? 0
+                     : (size_t)((long long)bs * np.T * np.S * slot_floats_narrow() * (long long)sizeof(float));
   const int mt = dtype == DDTREE_BF16 ? MT_BF16 : MT_F32;
   const long long T_max = ((long long)max_q_len * num_heads + mt - 1) / mt;
   long long slots = 0;
@@ -402,6 +407,33 @@ extern "C" size_t ddtree_verify_attn_workspace_size(int bs, int num_heads, int m
   }
   const long long sf = dtype == DDTREE_BF16 ? slot_floats_bf16(mt) : slot_floats(mt);
   return (size_t)(slots * sf * (long long)sizeof(float));
+}
+
+extern "C" int ddtree_verify_attn_plan(int bs, int num_heads, int max_q_len, int max_kv_len,
+                                       int num_splits, int dtype, int* tile_rows, int* splits) {
+  ddtree::clear_error();
+  DDTREE_REQUIRE(tile_rows && splits, DDTREE_EINVAL, "verify_attn_plan: null output");
+  DDTREE_REQUIRE(bs >= 0 && num_heads >= 1 && max_q_len >= 1 && max_kv_len >= max_q_len &&
+                     num_splits >= 0,
+                 DDTREE_EINVAL, "verify_attn_plan: invalid sizes");
+  DDTREE_REQUIRE(dtype == DDTREE_F32 || dtype == DDTREE_BF16, DDTREE_EINVAL,
+                 "verify_attn_plan: unknown dtype %d", dtype);
+  if (dtype == DDTREE_F32) {
+    *tile_rows = MT_F32;
+    *splits = num_splits == 0 ? 1 : num_splits;
+    return DDTREE_OK;
+  }
+  const int G = bf16_grid();
+  DDTREE_REQUIRE(G > 0, DDTREE_EHIP, "verify_attn_plan: cannot query the device compute units");
+  NarrowPlan np;
+  if (num_splits == 0 && narrow_plan(bs, num_heads, max_q_len, max_kv_len, G, np)) {
+    *tile_rows = MT_NARROW;
+    *splits = np.S;
+  } else {
+    *tile_rows = MT_BF16;
+    *splits = num_splits;
+  }
+  return DDTREE_OK;
 }
 
 namespace {
@@ -478,6 +510,16 @@ int verify_attn_impl(const char* fn, int L, const void* q, long long q_ls, const
     int rc = launch_f32(p, (int)(bs * T_max * p.S), s);
     if (rc != DDTREE_OK || p.S == 1) return rc;
     return launch_merge(p, mt, 0, dtype, s);
+  }
+  NarrowPlan np;
+  if (num_splits == 0 && narrow_plan(bs, num_heads, max_q_len, max_kv_len, bf16_grid(), np)) {
+    // few work units: 32-row tiles over a fixed split of the KV range, all
+    // layers side by side on grid y
+    DDTREE_REQUIRE((long long)bs * np.T * np.S * 32 < (1LL << 31), DDTREE_EUNSUPPORTED,
+                   "%s: grid too large", fn);
+    p.T_max = np.T;
+    p.S = np.S;
+    return launch_narrow(p, s);
   }
   p.S = num_splits;
   int G;

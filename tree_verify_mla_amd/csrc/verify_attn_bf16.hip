@@ -60,6 +60,7 @@
 #include <climits>
 
 #include "attn_common.h"
+#include "attn_device.h"
 #include "common.h"
 
 namespace ddtree {
@@ -67,23 +68,12 @@ namespace attn {
 
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-typedef short __attribute__((ext_vector_type(4))) i16x4_t;
-typedef uint32_t __attribute__((ext_vector_type(4))) u32x4_t;
-typedef __attribute__((address_space(3))) char lds_char;
+using namespace dev;
 
 constexpr int NWAVE = 4;           // waves per workgroup, 32 own rows each
-constexpr int ROWB = LATENT * 2;   // 1152 bytes per latent row
-constexpr int BUFB = KB * ROWB;    // 36864 bytes per block buffer
 constexpr int LOADS = BUFB / 1024; // 36 one-KB groups per block
 constexpr int LPW = LOADS / NWAVE; // gather loads per wave per block
 constexpr int NBUF = 4;            // block buffers (a power of two)
-constexpr int KS = LATENT / 16;    // 36 score k-steps of 16 features
 constexpr int RG = 4;              // 32-row groups of the tile
 constexpr int FB = 4;              // 32-feature output blocks per wave
 constexpr int KDEPTH = 4;          // score fragments read ahead
@@ -96,65 +86,6 @@ constexpr int TAB_REQ = 64;                  // requests the table holds
 constexpr int LDS_BYTES = TABB + 4 * TAB_REQ * 4 + 2 * TAB_REQ * 8;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(3 * (LPW - 1) + 1 < SYNC_STEP, "gathers are issued before the mid-block barrier");
-constexpr float LN2 = 0.693147180559945309f;
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14)
-constexpr int waitcnt_imm(int vm, int lgkm) {
-  return (vm & 15) | (7 << 4) | (lgkm << 8) | ((vm >> 4) << 14);
-}
-constexpr int VM_ANY = 63;
-
-// Workgroup barrier after an explicit wait (an s_waitcnt immediate).  The
-// empty asm statements with a memory clobber keep the compiler from moving
-// any memory access across the barrier (the barrier builtin alone does not
-// order memory for the optimiser); they emit nothing.
-template <int WAITCNT>
-__device__ inline void barrier_after() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(WAITCNT);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-template <int I, int N, typename F>
-__device__ inline void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-__device__ inline long long uni64(long long x) {
-  const int lo = __builtin_amdgcn_readfirstlane((int)(x & 0xffffffffLL));
-  const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
-  return ((long long)hi << 32) | (unsigned int)lo;
-}
-
-// Every lane computed the same request geometry from the same loads; saying
-// so lets the compiler keep it in scalar registers and branch on it.
-__device__ inline Geom uniform(Geom g) {
-  g.q0 = uni(g.q0); g.Q = uni(g.Q); g.kv0 = uni(g.kv0); g.N = uni(g.N);
-  g.P = uni(g.P); g.R = uni(g.R); g.T = uni(g.T); g.NB = uni(g.NB);
-  return g;
-}
-
-template <typename T>
-__device__ inline T lds_ld(const lds_char* p) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
-}
-template <typename T>
-__device__ inline void lds_st(lds_char* p, const T& v) {
-  *reinterpret_cast<__attribute__((address_space(3))) T*>(p) = v;
-}
-
-__device__ inline bf16x4_t lds_read_tr(const lds_char* p) {
-  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(const_cast<lds_char*>(p)));
-  return __builtin_bit_cast(bf16x4_t, v);
-}
 
 // Register files.  The 256 output accumulators fill the AGPRs; the score
 // accumulator, which the softmax reads, lives in VGPRs with the queries and
@@ -179,20 +110,6 @@ template <typename T>
 __device__ inline void here(T& x) {
   asm volatile("" : "+v"(x));
 }
-// max of three floats without the NaN-quieting that fmaxf adds in IEEE mode
-// (the scores are finite or -inf)
-__device__ inline float max3(float a, float b, float c) {
-  float r;
-  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-__device__ inline float other_half(float x) {
-  // value of lane l ^ 32
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
-}
-
 // BUF: the pool is addressed through a buffer resource (32-bit offsets,
 // pools under 4 GiB).  The gathers are then buffer_load ... lds, which the
 // compiler's wait-count tracking keeps apart from LDS reads, so the LDS
@@ -220,32 +137,15 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
       0x00020000);  // gfx9 raw buffer: untyped, no swizzle
 
   // ---- lane constants of the buffer layout (header comment) ----
-  // score fragment of k-step j at kofs[j & 1] + 2048 (j >> 1)
-  // (row l32 = 16 (l32 >> 4) + u, chunk 2j + hl)
-  int kofs0, kofs1;
-  {
-    const int u = l32 & 15;
-    const int kb = 1024 * (l32 >> 4) + 64 * u;
-    kofs0 = kb + 16 * ((hl + (u >> 2)) & 3);
-    kofs1 = kb + 16 * ((2 + hl + (u >> 2)) & 3);
-  }
-  // value fragments of global output block f (features 32f .. 32f+31), column
-  // half k2, row quad t at vofs[t] + 2048 f + 1024 k2: in 16-lane group g,
-  // lane c supplies block row 16 k2 + 8 t + 4 (l >> 5) + (c >> 2), features
-  // 32 f + 16 (g & 1) + 4 (c & 3) .. +3; after the transpose lane l holds
-  // feature 32 f + (l & 31) of rows 16 k2 + 8 t + 4 (l >> 5) + 0..3.
-  // This wave's blocks are f = 4 wave + fb; the 8 KB wave offset is folded in.
+  int kofs0, kofs1;  // score fragment of k-step j at kofs[j & 1] + 2048 (j >> 1)
+  score_offsets(lane, kofs0, kofs1);
+  // value fragments of global output block f at vofs[t] + 2048 f + 1024 k2;
+  // this wave's blocks are f = 4 wave + fb
   int vofs0, vofs1;
-  {
-    const int g16 = lane >> 4, cq = lane & 15;
-    const int cp = 2 * (g16 & 1) + ((cq & 3) >> 1);  // chunk inside the group's 4
-    const int vb = 8192 * wave + 64 * (4 * hl + (cq >> 2)) + 8 * (cq & 1);
-    vofs0 = vb + 16 * ((cp + hl) & 3);
-    vofs1 = vb + 512 + 16 * ((cp + 2 + hl) & 3);
-  }
+  value_offsets(lane, wave, vofs0, vofs1);
   // gather: the block row this lane fetches and its byte offset in the row
   const int grow = 16 * (wave & 1) + (lane >> 2);
-  const int gofs = 16 * (((lane & 3) - (lane >> 4)) & 3) + 576 * (wave >> 1);
+  const int gofs = gather_row_offset(lane) + 576 * (wave >> 1);
   // Load i of a block fills group 2 (9 (wave >> 1) + i) + (wave & 1) from
   // row offset gofs + 64 i.  The immediate offset applies to the pool address
   // and the LDS address alike, so the LDS base (M0) is target - 64 i.
@@ -497,34 +397,8 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_bf16_kernel(Params p_all) {
       static_for<0, LPW>([&](auto ic) { gather_one(base, src, ic); });
     };
 
-    // visibility of block blk's 32 columns to this lane's row (bit c =
-    // column blk * KB + c); nothing past the segment is visible
-    auto mask_word = [&](int blk) -> uint32_t {
-      const int cb = blk * KB;
-      const int ncol = g.N - cb;  // columns of the block that exist
-      if (blk >= b_end || ncol <= 0) return 0u;
-      const int jbase = cb - g.P;  // tree index of the block's column 0
-      uint32_t m32;
-      if (jbase >= 0) {
-        const int w0 = jbase >> 5, sh = jbase & 31;
-        uint32_t lo, hi;
-        if (p.W <= 4) {
-          lo = w0 == 0 ? vw[0] : (w0 == 1 ? vw[1] : (w0 == 2 ? vw[2] : vw[3]));
-          hi = w0 == 0 ? vw[1] : (w0 == 1 ? vw[2] : (w0 == 2 ? vw[3] : 0u));
-        } else {  // trees of more than 128 nodes
-          lo = w0 < p.W ? vrow[w0] : 0u;
-          hi = w0 + 1 < p.W ? vrow[w0 + 1] : 0u;
-        }
-        m32 = sh == 0 ? lo : (lo >> sh) | (hi << (32 - sh));
-      } else if (jbase <= -KB) {  // prefix columns only
-        m32 = 0xffffffffu;
-      } else {  // prefix columns 0 .. -jbase-1, then tree nodes 0, 1, ...
-        const int np = -jbase;
-        m32 = (0xffffffffu >> (32 - np)) | (vw[0] << np);
-      }
-      if (ncol < 32) m32 &= (1u << ncol) - 1u;
-      return m32;
-    };
+    // visibility of block blk's 32 columns to this lane's row
+    auto mask_word = [&](int blk) -> uint32_t { return dev::mask_word(blk, b_end, g, p.W, vw, vrow); };
 
     // ------------------------------------------------------------------
     // Softmax of one block of the own rows, in stages (each sits under one
