@@ -42,10 +42,12 @@ constexpr int KAPPA = 8;        // virtual units ahead of every tile (cost of a 
 constexpr int MT_BF16 = 128;    // rows per tile, bf16 matrix-core kernel (4 waves x 32 rows)
 constexpr int MT_F32 = 4;       // rows per tile, fp32 kernel
 constexpr int MT_NARROW = 32;   // rows per tile, bf16 kernel for small problems
-// The small-problem kernel serves single-layer bf16 calls whose 128-row work
-// units (tile x KV block, host bounds) number at most NARROW_UNITS_PER_CU per
-// compute unit.  Its split count S gives every workgroup the fewest steps of
-// NARROW_STEP blocks that at most one workgroup per compute unit allows.
+// The small-problem kernel serves bf16 calls whose 128-row work units (tile
+// x KV block, host bounds) number at most NARROW_UNITS_PER_CU per compute
+// unit.  Part s of every tile runs on XCD s % 8; the split count S is the
+// largest that keeps one workgroup per compute unit on every XCD, but no
+// larger than half the blocks (at least two blocks per part; ranges of up
+// to NARROW_STEP blocks run whole, S = 1).
 constexpr int NARROW_UNITS_PER_CU = 4;
 constexpr int NARROW_STEP = 4;
 
@@ -91,9 +93,9 @@ __host__ __device__ constexpr long long slot_floats(int mt) { return (long long)
 __host__ __device__ constexpr long long slot_floats_bf16(int mt) { return (long long)mt * (DV / 2 + 2 + 4); }
 
 // floats per partial slot of the small-problem kernel: O / l [32][512] in
-// fp16 (scaled per row and 128-feature quarter), m [32], l [32], inverse
-// scales [4][32]
-__host__ __device__ constexpr long long slot_floats_narrow() { return (long long)MT_NARROW * (DV / 2 + 2 + 4); }
+// fp16 (scaled per row and 128-feature quarter), then {m, l, inverse scale,
+// 0} [4 quarters][32 rows]
+__host__ __device__ constexpr long long slot_floats_narrow() { return (long long)MT_NARROW * (DV / 2 + 16); }
 
 // Split plan of the small-problem kernel from the host bounds; false when
 // the call takes the 128-row kernel.  G = compute units.
@@ -108,11 +110,10 @@ inline bool narrow_plan(int bs, int H, int max_q_len, int max_kv_len, int G, Nar
   if ((long long)bs * t128 * nb > (long long)NARROW_UNITS_PER_CU * G) return false;
   const long long t32 = ((long long)max_q_len * H + MT_NARROW - 1) / MT_NARROW;
   const long long tiles = (long long)bs * t32;
-  long long cap = G / tiles;  // ranges per tile that keep one workgroup per compute unit
-  if (cap < 1) cap = 1;
-  const long long steps = (nb + NARROW_STEP * cap - 1) / (NARROW_STEP * cap);
-  long long S = (nb + NARROW_STEP * steps - 1) / (NARROW_STEP * steps);
-  if (S < 1) S = 1;
+  long long per_xcd = (G / 8) / tiles;  // parts per tile on one XCD, one workgroup per compute unit
+  if (per_xcd < 1) per_xcd = 1;
+  long long S = nb <= NARROW_STEP ? 1 : (nb + 1) / 2;
+  if (S > 8 * per_xcd) S = 8 * per_xcd;
   np.T = (int)t32;
   np.S = (int)S;
   return true;

@@ -515,7 +515,7 @@ int verify_attn_impl(const char* fn, int L, const void* q, long long q_ls, const
   if (num_splits == 0 && narrow_plan(bs, num_heads, max_q_len, max_kv_len, bf16_grid(), np)) {
     // few work units: 32-row tiles over a fixed split of the KV range, all
     // layers side by side on grid y
-    DDTREE_REQUIRE((long long)bs * np.T * np.S * 32 < (1LL << 31), DDTREE_EUNSUPPORTED,
+    DDTREE_REQUIRE((long long)bs * np.T * (np.S + 7 + 32) < (1LL << 31), DDTREE_EUNSUPPORTED,
                    "%s: grid too large", fn);
     p.T_max = np.T;
     p.S = np.S;

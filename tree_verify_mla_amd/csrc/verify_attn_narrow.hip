@@ -48,6 +48,7 @@ constexpr int LSUM_N = RED_N + NW * 32 * 4; // row sums [wave][32] f32
 constexpr int LDS_N = LSUM_N + NW * 32 * 4;
 static_assert(LDS_N <= 160 * 1024, "LDS budget");
 constexpr float RESCALE_SLACK = 8.f;  // log2 units the block max may exceed the reference
+constexpr int KDN = 6;  // score fragments read ahead
 
 template <bool BUF>
 __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
@@ -59,17 +60,29 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
+  // Workgroup i runs on XCD i % 8 (hardware round-robin); XCD x takes the
+  // parts s = x, x + 8, ... of every tile, so the tiles of one request read
+  // each KV block through one XCD's L2 instead of all eight
   const int S = p.S;
-  const int s = blockIdx.x % S;
-  const int t = (blockIdx.x / S) % p.T_max;
-  const int r = blockIdx.x / (S * p.T_max);
-  if (r >= p.bs) return;
+  const int x = blockIdx.x & 7;
+  const int k8 = blockIdx.x >> 3;
+  const int tiles = p.bs * p.T_max;
+  const int s = x + 8 * (k8 / tiles);
+  const int r = (k8 % tiles) / p.T_max;
+  const int t = (k8 % tiles) % p.T_max;
+  if (s >= S) return;
   const Geom g = uniform(geom(p.qo, p.kvp, r, p.H, MTN));
   if (t >= g.T) return;
   const int b0 = uni((int)((long long)s * g.NB / S));
   const int b1 = uni((int)((long long)(s + 1) * g.NB / S));
-  if (b0 >= b1) return;  // an empty range (NB < S): the merge skips it
-  const int nsteps = (b1 - b0 + NW - 1) / NW;
+  if (b0 >= b1) {
+    // an empty part (NB < S): its rows saw no column (m = -inf), so the
+    // merge needs no geometry to skip it
+    if (threadIdx.x < 4 * MTN)
+      p.ws[(((long long)r * p.T_max + t) * S + s) * slot_floats_narrow() + MTN * DV / 2 + 4 * threadIdx.x] =
+          -INFINITY;
+    return;
+  }
 
   const __bf16* __restrict__ qg = static_cast<const __bf16*>(p.q);
   const char* __restrict__ poolb = static_cast<const char*>(p.pool);
@@ -102,7 +115,9 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
   // range or the request gather valid rows that the mask hides
   const int32_t* kvi = p.kvi + g.kv0;
   const int nslot_m1 = (int)min(p.num_slots - 1, (long long)0x7fffffff);
-  auto load_idx = [&](int blk, int h) { return kvi[min(blk * KB + 16 * h + (lane >> 2), g.N - 1)]; };
+  auto load_idx = [&](int blk, int h) {
+    return kvi[min(max(blk * KB + 16 * h + (lane >> 2), 0), g.N - 1)];
+  };
   auto gather = [&](lds_char* dst, int sid0, int sid1) {
     asm volatile("" : "+v"(sid0), "+v"(sid1));  // the clamp below waits for the index loads here
     const int sids[2] = {min(max(sid0, 0), nslot_m1), min(max(sid1, 0), nslot_m1)};
@@ -128,8 +143,36 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
     }
   };
 
+  // ---- block order ----
+  // The range's blocks b0 + q, q = 0 .. n-1, are taken in order of q.  Step 0
+  // gives q = 0, 1, 2 to waves 0, 1, 2 (wave 3's buffer first stages the
+  // queries); step k >= 1 gives q = 4k - 1 to wave 3 and q = 4k + w to waves
+  // w < 3, so wave 3 gathers its first block while step 0 runs.  A wave whose
+  // q is past the range gathers nothing and skips its scores, and every
+  // wave's value product skips that block.
+  // Position q holds block b0 + (q + rot) % n: the tiles of one part start
+  // at different blocks (rot = 3 t mod n), so a block one tile takes in a
+  // later step was already brought into the XCD's L2 by another tile's first
+  // step.
+  const int n = b1 - b0;
+  const int nsteps = n <= 3 ? 1 : 1 + (n - 3 + NW - 1) / NW;
+  const int rot = (3 * t) % n;
+  auto pos_of = [](int k, int w) { return NW * k + (w == 3 ? -1 : w); };
+  auto block_at = [&](int q) { return b0 + (q + rot) % n; };  // q >= 0
+  auto live = [&](int k, int w) {
+    const int q = pos_of(k, w);
+    return q >= 0 && q < n;
+  };
+
   // ---- prologue: slots of the first blocks, the queries through buffer 3 ----
-  int i0 = load_idx(b0 + wave, 0), i1 = load_idx(b0 + wave, 1);
+  const int b_first = block_at(wave == 3 ? 3 : wave);
+  int i0 = load_idx(b_first, 0), i1 = load_idx(b_first, 1);
+  // The slots and the ancestor words are taken before the queries' loads go
+  // out: the compiler waits for every outstanding load at a load's first use,
+  // and the first gathers would otherwise queue behind the queries.
+#pragma unroll
+  for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(vw[k]));
+  asm volatile("" : "+v"(i0), "+v"(i1));
   {
     // wave w stages groups 2 (9 (w >> 1) + i) + (w & 1), i < 9, of the query
     // tile (tile row 16 (w & 1) + lane / 4; rows past the request: its last)
@@ -145,20 +188,26 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
     });
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (wave < 3) gather(own, i0, i1);
+  const bool gather0 = wave < 3 && live(0, wave);
+  if (gather0) gather(own, i0, i1);
   __builtin_amdgcn_sched_barrier(0);
   // the query tile has landed for every wave (waves 0-2 may still gather)
-  if (wave < 3) {
+  if (gather0) {
     barrier_after<waitcnt_imm(36, 0)>();
   } else {
     barrier_after<waitcnt_imm(0, 0)>();
   }
-  bf16x8_t qf[KS];  // B operand of k-step j: features 16 j + 8 hl .. +7 of row l32
+  // B operand of k-step j: features 16 j + 8 hl .. +7 of row l32.  Held in
+  // AGPRs (matrix-core operands may come from either file), which leaves the
+  // VGPRs to the fragments read ahead in the loops below.
+  // (all reads issued before the first pin, which waits for its operand)
+  bf16x8_t qf[KS];
 #pragma unroll
-  for (int k = 0; k < KS; ++k)
-    qf[k] = lds_ld<bf16x8_t>(lds + 3 * BUFB + (k & 1 ? kofs1 : kofs0) + 2048 * (k >> 1));
+  for (int k = 0; k < KS; ++k) qf[k] = lds_ld<bf16x8_t>(lds + 3 * BUFB + (k & 1 ? kofs1 : kofs0) + 2048 * (k >> 1));
+#pragma unroll
+  for (int k = 0; k < KS; ++k) asm volatile("" : "+a"(qf[k]));
   barrier_after<waitcnt_imm(VM_ANY, 0)>();  // buffer 3 is free
-  if (wave == 3) gather(own, i0, i1);
+  if (wave == 3 && live(1, 3)) gather(own, i0, i1);
   __builtin_amdgcn_sched_barrier(0);
 
   f32x16_t o[4];  // O^T: features 128 wave + 32 fb .. +31 of row l32
@@ -169,33 +218,44 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
   float l_run = 0.f;        // this wave's columns' share of the row sum
 
   for (int k = 0; k < nsteps; ++k) {
-    const int blk = b0 + NW * k + wave;
-    if (k > 0) gather(own, i0, i1);
+    const bool mine = live(k, wave);
+    const int blk = block_at(max(pos_of(k, wave), 0));
+    if (mine && k > 0 && !(wave == 3 && k == 1)) gather(own, i0, i1);
     __builtin_amdgcn_sched_barrier(0);
-    // slots for the next step (past the end: clamped, unused)
-    i0 = load_idx(blk + NW, 0);
-    i1 = load_idx(blk + NW, 1);
-    // this wave's block has landed (the gathers write LDS behind the
-    // compiler's back: no LDS read may move above this wait)
+    // slots of the next step's block (past the range: clamped, unused)
+    const int b_next = block_at(pos_of(k + 1, wave));
+    i0 = load_idx(b_next, 0);
+    i1 = load_idx(b_next, 1);
+    // this wave's block has landed: every load but the two slot loads just
+    // issued (cold reads, left in flight) is done.  The gathers write LDS
+    // behind the compiler's back: no LDS read may move above this wait.
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    if (mine) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2, 15));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
-    // scores of the 32 rows against this wave's block
+    // scores of the 32 rows against this wave's block, the fragments read
+    // KDN steps ahead; lane (l32, hl) holds columns 8 (x >> 2) + 4 hl + (x & 3)
+    // of row l32
     f32x16_t sc = f32x16_t{};
+    float mb = -INFINITY;
+    if (mine) {
+      bf16x8_t kf[KS];
+      auto kread = [&](int j) { return lds_ld<bf16x8_t>(own + (j & 1 ? kofs1 : kofs0) + 2048 * (j >> 1)); };
+      static_for<0, KDN>([&](auto jc) { kf[jc] = kread(jc); });
+      static_for<0, KS>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j + KDN < KS) kf[j + KDN] = kread(j + KDN);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j], sc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      const uint32_t vis = mask_word(blk, b1, g, p.W, vw, vrow) >> (4 * hl);
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      const bf16x8_t kf = lds_ld<bf16x8_t>(own + (j & 1 ? kofs1 : kofs0) + 2048 * (j >> 1));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j], sc, 0, 0, 0);
+      for (int x = 0; x < 16; ++x)
+        if (!((vis >> (8 * (x >> 2) + (x & 3))) & 1u)) sc[x] = -INFINITY;
+      mb = max3(max3(sc[0], sc[1], sc[2]), max3(sc[3], sc[4], sc[5]), max3(sc[6], sc[7], sc[8]));
+      mb = max3(max3(sc[9], sc[10], sc[11]), max3(sc[12], sc[13], sc[14]), max3(sc[15], mb, mb));
     }
-    // lane (l32, hl) holds columns 8 (x >> 2) + 4 hl + (x & 3) of row l32
-    const uint32_t mine = mask_word(blk, b1, g, p.W, vw, vrow) >> (4 * hl);
-#pragma unroll
-    for (int x = 0; x < 16; ++x)
-      if (!((mine >> (8 * (x >> 2) + (x & 3))) & 1u)) sc[x] = -INFINITY;
-    float mb = max3(max3(sc[0], sc[1], sc[2]), max3(sc[3], sc[4], sc[5]), max3(sc[6], sc[7], sc[8]));
-    mb = max3(max3(sc[9], sc[10], sc[11]), max3(sc[12], sc[13], sc[14]), max3(sc[15], mb, mb));
     mb = fmaxf(mb, other_half(mb));
     if (hl == 0) lds_st(red + 128 * wave + 4 * l32, mb);
     barrier_after<waitcnt_imm(VM_ANY, 0)>();
@@ -210,43 +270,51 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
     const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
-    const float mu = m_run == -INFINITY ? 0.f : m_run;
-    uint32_t pw[8];
+    if (mine) {
+      const float mu = m_run == -INFINITY ? 0.f : m_run;
+      uint32_t pw[8];
 #pragma unroll
-    for (int x = 0; x < 16; x += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[x], c, -mu));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[x + 1], c, -mu));
-      l_run += e0 + e1;
-      const bf16x2_t two = {(__bf16)e0, (__bf16)e1};
-      pw[x >> 1] = __builtin_bit_cast(uint32_t, two);
+      for (int x = 0; x < 16; x += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[x], c, -mu));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[x + 1], c, -mu));
+        l_run += e0 + e1;
+        const bf16x2_t two = {(__bf16)e0, (__bf16)e1};
+        pw[x >> 1] = __builtin_bit_cast(uint32_t, two);
+      }
+      // P^T in the B-operand layout of the value product: k-step 0 holds
+      // columns x = 0..7 of the lane, k-step 1 x = 8..15
+      lds_st(pbuf + 2048 * wave + 16 * lane, __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]}));
+      lds_st(pbuf + 2048 * wave + 1024 + 16 * lane,
+             __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]}));
     }
-    // P^T in the B-operand layout of the value product: k-step 0 holds
-    // columns x = 0..7 of the lane, k-step 1 x = 8..15
-    lds_st(pbuf + 2048 * wave + 16 * lane, __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]}));
-    lds_st(pbuf + 2048 * wave + 1024 + 16 * lane,
-           __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]}));
     if (alpha != 1.f) {
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) o[fb] *= alpha;
     }
     barrier_after<waitcnt_imm(VM_ANY, 0)>();
 
-    // values: this wave's 128 features over the step's four blocks
-#pragma unroll
-    for (int sb = 0; sb < NW; ++sb) {
+    // values: this wave's 128 features over the step's live blocks, in order
+    // of q (step 0: waves 0, 1, 2; later steps: 3, 0, 1, 2 -- a prefix of
+    // that order is live); per block both P^T fragments and all eight value
+    // fragments are read before its 8 MFMAs
+    const int nlive = k == 0 ? min(n, 3) : min(max(n - pos_of(k, 3), 0), NW);
+    for (int i = 0; i < nlive; ++i) {
+      const int sb = k == 0 ? i : (i + 3) & 3;
       const lds_char* vb = lds + sb * BUFB;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8_t pf = lds_ld<bf16x8_t>(pbuf + 2048 * sb + 1024 * k2 + 16 * lane);
-#pragma unroll
-        for (int fb = 0; fb < 4; ++fb) {
-          const int off = 2048 * fb + 1024 * k2;
-          const bf16x4_t lo = lds_read_tr(vb + vofs0 + off);
-          const bf16x4_t hi = lds_read_tr(vb + vofs1 + off);
-          const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[fb], 0, 0, 0);
-        }
-      }
+      bf16x8_t pf[2], vf[8];
+      pf[0] = lds_ld<bf16x8_t>(pbuf + 2048 * sb + 16 * lane);
+      pf[1] = lds_ld<bf16x8_t>(pbuf + 2048 * sb + 1024 + 16 * lane);
+      static_for<0, 8>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;  // k-step j >> 2, feature block j & 3
+        const int off = 1024 * (j >> 2) + 2048 * (j & 3);
+        const bf16x4_t lo = lds_read_tr(vb + vofs0 + off);
+        const bf16x4_t hi = lds_read_tr(vb + vofs1 + off);
+        vf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      });
+      static_for<0, 8>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j >> 2], o[j & 3], 0, 0, 0);
+      });
     }
     // every wave is done with the buffers, P^T and the maxima
     barrier_after<waitcnt_imm(VM_ANY, 0)>();
@@ -290,8 +358,9 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
   // accumulators' lane layout -- store (fb, gp) of wave w writes 1 KB at half
   // offset ((4 w + fb) 2 + gp) 512, lane l's 16 bytes holding features
   // 128 w + 32 fb + 16 gp + 4 (l >> 5) .. +3 and the same + 8 of row l & 31 --
-  // then m [32], l [32] and the inverse scales [4][32] in fp32.  A row that
-  // saw no column (l = 0, m = -inf) stores zeros; the merge skips it.
+  // then per feature quarter and row {m, l, inverse scale, 0} in fp32 (one
+  // 16-byte load per part in the merge).  A row that saw no column (l = 0,
+  // m = -inf) stores zeros; the merge skips it.
   float* base = p.ws + (((long long)r * p.T_max + t) * S + s) * slot_floats_narrow();
   float* stats = base + MTN * DV / 2;
   _Float16* ob = reinterpret_cast<_Float16*>(base) + (size_t)wave * (4 * 2 * 512) + 8 * lane;
@@ -315,13 +384,8 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
       for (int e = 0; e < 8; ++e) v8[e] = (_Float16)(o[fb][8 * gp + e] * f);
       *reinterpret_cast<f16x8_t*>(ob + (fb * 2 + gp) * 512) = v8;
     }
-  if (hl == 0) {
-    stats[2 * MTN + wave * MTN + l32] = ldexpf(1.f, ex - 15);
-    if (wave == 0) {
-      stats[l32] = M;
-      stats[MTN + l32] = L;
-    }
-  }
+  if (hl == 0)
+    *reinterpret_cast<f32x4_t*>(stats + 4 * (wave * MTN + l32)) = f32x4_t{M, L, ldexpf(1.f, ex - 15), 0.f};
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -331,8 +395,7 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
 // l_j 2^(m_j - M), its values times their inverse scale).  The slots' places
 // do not depend on the request's offsets, so their loads and the offsets'
 // go out together.
-constexpr int NM_BATCH = 8;  // ranges whose loads are in flight together
-
+template <int NM_BATCH>  // parts whose loads are in flight together
 __global__ __launch_bounds__(64) void merge_narrow_kernel(Params p_all) {
   const Params p = at_layer(p_all);
   const int run = blockIdx.x & 31, tile = blockIdx.x >> 5;
@@ -342,44 +405,52 @@ __global__ __launch_bounds__(64) void merge_narrow_kernel(Params p_all) {
   const int w = run >> 3;  // feature quarter of the run
   const long long sf = slot_floats_narrow();
   const float* slot0 = p.ws + ((long long)r * p.T_max + t) * p.S * sf;
-  const Geom g = geom(p.qo, p.kvp, r, p.H, MT_NARROW);
   float M = -INFINITY, L = 0.f;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int j0 = 0; j0 < p.S; j0 += NM_BATCH) {
-    float ms[NM_BATCH], ls[NM_BATCH], us[NM_BATCH];
-    f16x8_t x[NM_BATCH];
+  f32x4_t st[NM_BATCH];  // {m, l, inverse scale, 0} of the lane's row and quarter
+  f16x8_t x[NM_BATCH];
+  // Two loads per part (a wave keeps at most 63 in flight).  No load is
+  // conditional (a branch around a load makes the compiler wait for every
+  // load before it): parts past S reread the last one, unused.
+  auto load_batch = [&](int j0) {
 #pragma unroll
     for (int j = 0; j < NM_BATCH; ++j) {
-      if (j0 + j < p.S) {
-        const float* base = slot0 + (long long)(j0 + j) * sf;
-        const float* stats = base + MT_NARROW * DV / 2;
-        ms[j] = stats[l32];
-        ls[j] = stats[MT_NARROW + l32];
-        us[j] = stats[(2 + w) * MT_NARROW + l32];
-        x[j] = *reinterpret_cast<const f16x8_t*>(reinterpret_cast<const _Float16*>(base) + run * 512 + 8 * lane);
-      }
+      const float* base = slot0 + (long long)min(j0 + j, p.S - 1) * sf;
+      st[j] = *reinterpret_cast<const f32x4_t*>(base + MT_NARROW * DV / 2 + 4 * (w * MT_NARROW + l32));
+      x[j] = *reinterpret_cast<const f16x8_t*>(reinterpret_cast<const _Float16*>(base) + run * 512 + 8 * lane);
     }
-    if (t >= g.T) return;
+  };
+  auto fold_batch = [&](int j0) {
 #pragma unroll
     for (int j = 0; j < NM_BATCH; ++j) {
-      const int s = j0 + j;
-      if (s >= p.S) continue;
-      // ranges with no block (NB < S) were never written
-      if ((long long)s * g.NB / p.S >= (long long)(s + 1) * g.NB / p.S) continue;
-      if (ms[j] == -INFINITY) continue;  // the row saw no column in this range
-      const float Mn = fmaxf(M, ms[j]);
+      if (j0 + j >= p.S) continue;
+      const float mj = st[j][0];
+      if (mj == -INFINITY) continue;  // the row saw no column in this part (or none at all)
+      const float Mn = fmaxf(M, mj);
       const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
-      const float wj = ls[j] * exp2f(ms[j] - Mn);
-      const float wv = wj * us[j];
+      const float wj = st[j][1] * exp2f(mj - Mn);
+      const float wv = wj * st[j][2];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a + (float)x[j][e] * wv;
       L = L * a + wj;
       M = Mn;
     }
+  };
+  load_batch(0);
+  // the request's offsets are read after the first parts' loads are issued
+  // (nothing moves across this statement), so both are in flight together
+  asm volatile("" ::: "memory");
+  const Geom g = geom(p.qo, p.kvp, r, p.H, MT_NARROW);
+  fold_batch(0);
+  for (int j0 = NM_BATCH; j0 < p.S; j0 += NM_BATCH) {
+    load_batch(j0);
+    fold_batch(j0);
   }
-  if (t * MT_NARROW + l32 >= g.R) return;
+  // a tile past the request's end, or a row past it (its slots were never
+  // written)
+  if (t >= g.T || t * MT_NARROW + l32 >= g.R) return;
   const float inv = 1.f / L;
   // run (fb, gp) of quarter w: features 128 w + 32 fb + 16 gp + 4 hl .. +3 and + 8
   const int fb = (run >> 1) & 3, gp = run & 1;
@@ -398,15 +469,19 @@ __global__ __launch_bounds__(64) void merge_narrow_kernel(Params p_all) {
 }  // namespace
 
 int launch_narrow(const Params& p, hipStream_t s) {
-  const unsigned grid = (unsigned)((long long)p.bs * p.T_max * p.S);
+  // eight XCD columns of ceil(S / 8) parts x every tile
+  const unsigned grid = (unsigned)(8LL * ((p.S + 7) / 8) * p.bs * p.T_max);
   if (p.num_slots * (long long)ROWB <= 0xffffffffLL)
     hipLaunchKernelGGL((attn_narrow_kernel<true>), dim3(grid, p.L), dim3(NW * 64), 0, s, p);
   else
     hipLaunchKernelGGL((attn_narrow_kernel<false>), dim3(grid, p.L), dim3(NW * 64), 0, s, p);
   int rc = check_launch("verify_attn(narrow)");
   if (rc != DDTREE_OK || p.S == 1) return rc;
-  hipLaunchKernelGGL(merge_narrow_kernel, dim3((unsigned)((long long)p.bs * p.T_max * 32), p.L), dim3(64), 0, s,
-                     p);
+  const dim3 mgrid((unsigned)((long long)p.bs * p.T_max * 32), p.L);
+  if (p.S <= 8)
+    hipLaunchKernelGGL(merge_narrow_kernel<8>, mgrid, dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL(merge_narrow_kernel<24>, mgrid, dim3(64), 0, s, p);
   return check_launch("verify_attn(narrow merge)");
 }
 
