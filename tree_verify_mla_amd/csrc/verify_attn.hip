@@ -30,9 +30,14 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// fp32 path: one wavefront per query row, columns one at a time.  Lane k
-// owns latent entries k + 64j (9 of the 576 for the score, 8 of the 512
-// for the output).
+// fp32 path: one wavefront per query row.  Lane k owns latent entries
+// k + 64j (9 of the 576 for the score, 8 of the 512 for the output).  The
+// columns are taken 64 at a time: one round trip brings every column's slot
+// and visibility (a lane each), then the visible columns go in groups of
+// CG, all their rows' loads in flight together, and one online-softmax
+// update per group (base 2, running max m, running sum l).
+constexpr int CG = 16;
+
 __global__ __launch_bounds__(256) void attn_f32_kernel(Params p_all) {
   const Params p = at_layer(p_all);
   const int S = p.S;
@@ -59,25 +64,59 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Params p_all) {
   float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) o[k] = 0.f;
-  for (int c = c0; c < c1; ++c) {
-    if (c >= g.P) {
-      const int j = c - g.P;
-      if ((j >> 5) >= p.W || !((vrow[j >> 5] >> (j & 31)) & 1u)) continue;
+  for (int cb = c0; cb < c1; cb += 64) {
+    // column cb + lane: its slot (clamped into the pool) and whether this
+    // row sees it (prefix columns always, tree column P + j iff bit j of the
+    // row's ancestor bitset); no load is conditional
+    const int cl = cb + lane;
+    long long sl = p.kvi[g.kv0 + min(cl, g.N - 1)];
+    sl = sl < 0 ? 0 : (sl >= p.num_slots ? p.num_slots - 1 : sl);
+    const int j = cl - g.P;
+    const uint32_t word = vrow[min(max(j, 0) >> 5, p.W - 1)];
+    const bool vis = cl < c1 && (j < 0 || ((j >> 5) < p.W && ((word >> (j & 31)) & 1u)));
+    unsigned long long todo = __ballot(vis);
+    while (todo) {
+      // the next CG visible columns (a short group repeats its first)
+      int col[CG];
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        col[u] = todo ? __ffsll((long long)todo) - 1 : col[0];
+        cnt += todo ? 1 : 0;
+        todo &= todo - 1;
+      }
+      float kv[CG][9];
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        const long long su = __shfl(sl, col[u]);
+        const float* row = pool + su * LATENT;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) kv[u][k] = row[lane + 64 * k];
+      }
+      float sv[CG];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        float d = 0.f;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) d = fmaf(qv[k], kv[u][k], d);
+        sv[u] = wave_sum(d) * p.scale_log2;
+        if (u < cnt) mx = fmaxf(mx, sv[u]);
+      }
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] *= alpha;
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        const float pw = u < cnt ? exp2f(sv[u] - mn) : 0.f;
+        l += pw;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = fmaf(pw, kv[u][k], o[k]);
+      }
+      m = mn;
     }
-    long long slot = p.kvi[g.kv0 + c];
-    slot = slot < 0 ? 0 : (slot >= p.num_slots ? p.num_slots - 1 : slot);
-    const float* kv = pool + slot * LATENT;
-    float d = 0.f;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) d = fmaf(qv[k], kv[lane + 64 * k], d);
-    const float sv = wave_sum(d) * p.scale_log2;
-    const float mn = fmaxf(m, sv);
-    const float alpha = exp2f(m - mn);
-    const float pw = exp2f(sv - mn);
-    l = l * alpha + pw;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = fmaf(pw, kv[lane + 64 * k], o[k] * alpha);
-    m = mn;
   }
   const size_t orow = (size_t)g.q0 * p.H + rho;
   if (S == 1) {
