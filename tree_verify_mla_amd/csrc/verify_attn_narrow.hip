@@ -352,7 +352,8 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
       p.lse[(size_t)g.q0 * p.H + rho] = (M + log2f(L)) * LN2;
     return;
   }
-  // The partial: O / l of every row (a weighted mean of the c_kv rows the
+  // The partial (stored non-temporally: nothing on this XCD reads it again,
+  // and fewer dirty lines are left to write back when the kernel ends): O / l of every row (a weighted mean of the c_kv rows the
   // range saw) in fp16 after a power-of-two scale per row and feature quarter
   // that brings its largest magnitude into [2^14, 2^15), in the
   // accumulators' lane layout -- store (fb, gp) of wave w writes 1 KB at half
@@ -382,10 +383,10 @@ __global__ __launch_bounds__(NW * 64) void attn_narrow_kernel(Params p_all) {
       f16x8_t v8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) v8[e] = (_Float16)(o[fb][8 * gp + e] * f);
-      *reinterpret_cast<f16x8_t*>(ob + (fb * 2 + gp) * 512) = v8;
+      __builtin_nontemporal_store(v8, reinterpret_cast<f16x8_t*>(ob + (fb * 2 + gp) * 512));
     }
   if (hl == 0)
-    *reinterpret_cast<f32x4_t*>(stats + 4 * (wave * MTN + l32)) = f32x4_t{M, L, ldexpf(1.f, ex - 15), 0.f};
+    __builtin_nontemporal_store(f32x4_t{M, L, ldexpf(1.f, ex - 15), 0.f}, reinterpret_cast<f32x4_t*>(stats + 4 * (wave * MTN + l32)));
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
