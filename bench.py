@@ -79,7 +79,7 @@ def copy_probe(mib: int) -> None:
 
 
 ATTN_SOURCES = ("tree_verify_mla_amd/csrc/verify_attn_bf16.hip", "tree_verify_mla_amd/csrc/verify_attn.hip",
-                "tree_verify_mla_amd/csrc/attn_common.h")
+                "tree_verify_mla_amd/csrc/attn_common.h", "tree_verify_mla_amd/csrc/attn_device.h")
 COUNTERS = os.path.join(ROOT, "profiles", "verify_attn_h64_bs8_q33_p8192_counters.txt")
 
 

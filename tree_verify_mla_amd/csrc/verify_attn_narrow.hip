@@ -8,27 +8,28 @@
 // queries, a 32 KB partial) and the split is fixed by the host:
 //
 // Workgroup (r, t, s) = 4 wavefronts = tile t (32 rows) of request r, KV
-// blocks [s NB / S, (s+1) NB / S) (S splits).  The range is taken in steps of
-// four 32-column blocks.  In a step, wave w
-//   * gathers block 4k + w of the range into its own LDS buffer and forms
+// blocks [s NB / S, (s+1) NB / S) (S splits, part s on XCD s % 8).  The
+// range is taken in steps of up to four 32-column blocks.  In a step, wave w
+//   * gathers its block into its own LDS buffer and forms
 //     S^T[32 col x 32 row] = K . Q^T over the 576 latents (36 MFMAs
-//     32x32x16, the queries held in registers: the B operand of every step);
+//     32x32x16, the queries held in AGPRs: the B operand of every step);
 //   * after the four waves have put their block maxima in LDS, moves each
 //     row's softmax reference (the same decision in every wave), turns its
 //     scores into bf16 weights P^T and puts them in LDS;
-//   * accumulates output features 128w .. 128w+127 of all 32 rows over all
-//     four blocks: O^T[128 x 32] += V^T[128 x 128 col] . P^T[128 col x 32]
-//     (32 MFMAs, V^T read transposed from the four buffers).
-// A step costs three workgroup barriers and leaves its four buffers free for
-// the next step's gathers.  At the end the waves add their row sums; with one
-// range per tile (S = 1) the workgroup writes the bf16 output and lse, else a
+//   * accumulates output features 128w .. 128w+127 of all 32 rows over the
+//     step's blocks: O^T[128 x 32] += V^T[128 x 32 col] . P^T[32 col x 32]
+//     per block (8 MFMAs, V^T read transposed from the block's buffer).
+// A step costs three workgroup barriers and leaves its buffers free for the
+// next step's gathers.  At the end the waves add their row sums; with one
+// part per tile (S = 1) the workgroup writes the bf16 output and lse, else a
 // partial that merge_narrow_kernel folds by log-sum-exp ("The 30-Column Mask
 // ...", section "The Context: Building a Custom Verify Attention Kernel":
 // KV-split flash decoding with a partial reduction).
 //
 // The queries are staged through buffer 3 (a block's layout, so their
-// fragments are read like score fragments); wave 3 gathers its first block
-// once every wave has its queries.
+// fragments are read like score fragments); so the first step takes three
+// blocks and wave 3 gathers its first block (the part's fourth) while that
+// step runs.
 #include "attn_common.h"
 #include "attn_device.h"
 #include "common.h"
