@@ -15,6 +15,8 @@
 //   max m_c, its sum s_c of e^(x - m_c), and its k best (value, id), best
 //   first, by rounds of an argmax over the entries still in play (32-bit
 //   order keys, the smallest id among equal keys);
+//   (a row of one chunk -- vocabularies up to CHUNK -- is final there:
+//   the chunk writes x - lse and the ids itself and no merge runs);
 // * merge_kernel: one wavefront per row folds the chunks' (m_c, s_c) into
 //   M = max m_c and S = sum_c s_c e^(m_c - M), lse = M + log S, and takes
 //   the row's k best out of the chunks' candidates (the j-th best of a row
@@ -148,7 +150,8 @@ __device__ inline float to_f32(T x) {
 template <typename T, bool VEC, bool FULL>
 __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int vocab, int C, int k,
                                            float* __restrict__ ws_ms, float* __restrict__ ws_val,
-                                           int32_t* __restrict__ ws_id, int row, int c,
+                                           int32_t* __restrict__ ws_id, float* __restrict__ out_val,
+                                           int32_t* __restrict__ out_id, int row, int c,
                                            float* red_m, float* red_s, uint2 (*cand)[KMAX]) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const long long c0 = (long long)c * CHUNK;          // first element of the chunk in its row
@@ -259,14 +262,20 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
   }
   __syncthreads();
   if (wave != 0) return;
-  if (t == 0) {  // the workgroup's (max, sum), waves in order
-    float mc = red_m[0], sc = red_s[0];
-    lse_add(mc, sc, red_m[1], red_s[1]);
-    lse_add(mc, sc, red_m[2], red_s[2]);
-    lse_add(mc, sc, red_m[3], red_s[3]);
+  // the workgroup's (max, sum), waves in order
+  float mc = red_m[0], sc = red_s[0];
+  lse_add(mc, sc, red_m[1], red_s[1]);
+  lse_add(mc, sc, red_m[2], red_s[2]);
+  lse_add(mc, sc, red_m[3], red_s[3]);
+  if (t == 0 && C > 1) {
     ws_ms[2 * slot] = mc;
     ws_ms[2 * slot + 1] = sc;
   }
+  // A row of one chunk needs no merge: its log-sum-exp is the chunk's (the
+  // merge's fold of a single (max, sum) returns it exactly), and the chunk's
+  // k best, best first, are the row's.
+  const bool whole_row = C == 1;
+  const float lse = mc + __logf(sc);
   // wave 0: candidate i = (wave i / k, round i % k), two per lane
   uint32_t ck[2], cid[2];
   float cv[2];
@@ -287,13 +296,18 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
     uint32_t gk;
     const bool owner = wave_owner(lk, lid, gk);
     if (gk == 0u) {
-      if (lane == 0) {
+      if (lane == 0 && !whole_row) {
         ws_val[slot * k + r] = -INFINITY;
         ws_id[slot * k + r] = INT_MAX;
       }
     } else if (owner) {
-      ws_val[slot * k + r] = lv;
-      ws_id[slot * k + r] = (int32_t)lid;
+      if (whole_row) {
+        out_val[(size_t)row * k + r] = lv - lse;
+        out_id[(size_t)row * k + r] = (int32_t)lid;
+      } else {
+        ws_val[slot * k + r] = lv;
+        ws_id[slot * k + r] = (int32_t)lid;
+      }
       if (second) ck[1] = 0u; else ck[0] = 0u;
     }
   }
@@ -303,14 +317,18 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits, int vocab, int C,
                                                    int k, float* __restrict__ ws_ms,
                                                    float* __restrict__ ws_val,
-                                                   int32_t* __restrict__ ws_id) {
+                                                   int32_t* __restrict__ ws_id,
+                                                   float* __restrict__ out_val,
+                                                   int32_t* __restrict__ out_id) {
   __shared__ float red_m[CT / 64], red_s[CT / 64];
   __shared__ uint2 cand[CT / 64][KMAX];  // each wave's k best: (key, id)
   const int row = blockIdx.x / C, c = blockIdx.x % C;
   if ((long long)(c + 1) * CHUNK <= vocab)
-    chunk_body<T, VEC, true>(logits, vocab, C, k, ws_ms, ws_val, ws_id, row, c, red_m, red_s, cand);
+    chunk_body<T, VEC, true>(logits, vocab, C, k, ws_ms, ws_val, ws_id, out_val, out_id, row, c, red_m,
+                             red_s, cand);
   else
-    chunk_body<T, VEC, false>(logits, vocab, C, k, ws_ms, ws_val, ws_id, row, c, red_m, red_s, cand);
+    chunk_body<T, VEC, false>(logits, vocab, C, k, ws_ms, ws_val, ws_id, out_val, out_id, row, c, red_m,
+                              red_s, cand);
 }
 
 __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __restrict__ ws_ms,
@@ -470,21 +488,21 @@ extern "C" int ddtree_drafter_topk(const void* logits, int dtype, int rows, int 
     const float* x = static_cast<const float*>(logits);
     if (aligned && vocab % 4 == 0)
       hipLaunchKernelGGL((chunk_kernel<float, true>), grid, dim3(CT), 0, s, x, vocab, (int)C, topk,
-                         ws_ms, ws_val, ws_id);
+                         ws_ms, ws_val, ws_id, topk_logprobs, topk_ids);
     else
       hipLaunchKernelGGL((chunk_kernel<float, false>), grid, dim3(CT), 0, s, x, vocab, (int)C, topk,
-                         ws_ms, ws_val, ws_id);
+                         ws_ms, ws_val, ws_id, topk_logprobs, topk_ids);
   } else {
     const __bf16* x = static_cast<const __bf16*>(logits);
     if (aligned && vocab % 8 == 0)
       hipLaunchKernelGGL((chunk_kernel<__bf16, true>), grid, dim3(CT), 0, s, x, vocab, (int)C,
-                         topk, ws_ms, ws_val, ws_id);
+                         topk, ws_ms, ws_val, ws_id, topk_logprobs, topk_ids);
     else
       hipLaunchKernelGGL((chunk_kernel<__bf16, false>), grid, dim3(CT), 0, s, x, vocab, (int)C,
-                         topk, ws_ms, ws_val, ws_id);
+                         topk, ws_ms, ws_val, ws_id, topk_logprobs, topk_ids);
   }
   int rc = ddtree::check_launch("drafter_topk(chunks)");
-  if (rc != DDTREE_OK) return rc;
+  if (rc != DDTREE_OK || C == 1) return rc;  // rows of one chunk are final already
   hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(64), 0, s, (int)C, topk, ws_ms, ws_val, ws_id,
                      topk_logprobs, topk_ids);
   return ddtree::check_launch("drafter_topk(merge)");
