@@ -35,6 +35,8 @@ def test_plan_picks_the_narrow_kernel_for_small_calls():
     assert _lib.ddtree_verify_attn_plan(8, 64, 33, 8225, 0, _lib.DDTREE_BF16) == (128, 0)
     # a forced split keeps the 128-row kernel
     assert _lib.ddtree_verify_attn_plan(1, 8, 33, 4129, 7, _lib.DDTREE_BF16) == (128, 7)
+    # an empty batch is a valid call (the attention call returns at once)
+    assert _lib.ddtree_verify_attn_plan(0, 8, 33, 4129, 0, _lib.DDTREE_BF16) == (128, 0)
 
 
 @pytest.mark.parametrize("twin", [False, True])

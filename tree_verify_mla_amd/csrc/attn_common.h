@@ -104,7 +104,7 @@ struct NarrowPlan {
   int S;  // ranges per tile
 };
 inline bool narrow_plan(int bs, int H, int max_q_len, int max_kv_len, int G, NarrowPlan& np) {
-  if (G <= 0) return false;
+  if (G <= 0 || bs < 1 || H < 1 || max_q_len < 1) return false;
   const long long nb = ((long long)max_kv_len + KB - 1) / KB;
   const long long t128 = ((long long)max_q_len * H + MT_BF16 - 1) / MT_BF16;
   if ((long long)bs * t128 * nb > (long long)NARROW_UNITS_PER_CU * G) return false;
