@@ -35,6 +35,7 @@ constexpr int CHUNK = CT * EPT;    // logits per chunk
 constexpr int KMAX = 32;           // largest k
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr int MERGE_PER_LANE = 16; // chunk candidates per lane in the merge (C * k <= 1024)
+constexpr int STAGE = 64;          // a wave's logits at or above its threshold, staged in LDS
 
 // order-preserving map of a finite fp32 to uint32 (larger value -> larger key)
 __device__ inline uint32_t fkey(float f) {
@@ -152,7 +153,8 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
                                            float* __restrict__ ws_ms, float* __restrict__ ws_val,
                                            int32_t* __restrict__ ws_id, float* __restrict__ out_val,
                                            int32_t* __restrict__ out_id, int row, int c,
-                                           float* red_m, float* red_s, uint2 (*cand)[KMAX]) {
+                                           float* red_m, float* red_s, uint2 (*cand)[KMAX],
+                                           uint2 (*stage)[STAGE]) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const long long c0 = (long long)c * CHUNK;          // first element of the chunk in its row
   const int n = FULL ? CHUNK : (int)min((long long)CHUNK, vocab - c0);  // elements of the chunk
@@ -196,6 +198,7 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) m = fmaxf(m, x[j]);
+  const float lane_max = m;
   // e^(x - m) as 2^(x log2 e - m log2 e): one fused multiply-add per element
   const float mref = (m == -INFINITY ? 0.f : m) * LOG2E;
   float s = 0.f;
@@ -212,51 +215,109 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
   // The chunk's k best (the largest value, then the smallest id), in two
   // steps without a barrier per round.  Keys are 32-bit order keys; 0 means
   // nothing (every float's key is larger).
-  // 1. each wave takes its own k best.  A lane keeps its two best entries
-  //    (its registers hold ids in ascending order, so of equal keys the
-  //    first is the smaller id); a round is the wave maximum of the lanes'
-  //    first keys, then the smallest id among the lanes that hold it, and the
-  //    owner moves its second entry up.  A lane that has given up both looks
-  //    again, for the best entries after the last one it gave up in (key
-  //    descending, id ascending) order -- rare, and only that lane's wave
-  //    waits for it.
+  // 1. each wave takes its own k best, cand[wave][0 .. k-1].
+  //    Threshold form: the k-th largest of the lanes' maxima, tau, is at most
+  //    the wave's k-th largest logit (each of those k lanes holds a logit
+  //    >= tau), so the wave's k best are among its logits >= tau -- with
+  //    distinct values, little more than k of them.  tau comes from rounds
+  //    of a wave maximum over the lanes' maxima (the lanes holding a round's
+  //    maximum leave together, so equal maxima count once each); the logits
+  //    >= tau go to LDS, and each takes the place its rank among them gives
+  //    (the number of staged entries before it in the order).  The form
+  //    needs tau > -inf (a logit >= tau is then real: masked elements hold
+  //    -inf) and at most STAGE logits >= tau; a wave where either fails (a
+  //    run of equal or -inf logits) takes the general form below.
+  const uint32_t key_ninf = fkey(-INFINITY);
+  bool general = false;
+  {
+    uint32_t cur = fkey(lane_max), tk = 0u;
+    int got = 0;  // lanes whose maximum is >= tk
+    while (got < k) {
+      const uint32_t gk = wave_ext<true>(cur);
+      if (gk <= key_ninf) break;
+      got += (int)__popcll(__ballot(cur == gk));
+      cur = cur == gk ? 0u : cur;
+      tk = gk;
+    }
+    general = got < k;
+    if (!general) {
+      const float tau = funkey(tk);
+      int nw = 0;  // logits >= tau so far (wave-uniform)
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const bool pass = x[j] >= tau;
+        const uint64_t b = __ballot(pass);
+        if (b != 0ull) {
+          const int pos = nw + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+          if (pass && pos < STAGE)
+            stage[wave][pos] = make_uint2(fkey(x[j]), (uint32_t)(c0 + elem_of<T, VEC>(t, j)));
+          nw += (int)__popcll(b);
+        }
+      }
+      general = nw > STAGE;
+      if (!general) {
+        uint32_t mk = 0u, mid = 0xffffffffu;
+        if (lane < nw) {
+          const uint2 v = stage[wave][lane];
+          mk = v.x, mid = v.y;
+        }
+        int rank = 0;
+#pragma unroll 4
+        for (int i = 0; i < nw; ++i) {
+          const uint2 v = stage[wave][i];  // the same entry in every lane
+          rank += (int)((v.x > mk) | ((v.x == mk) & (v.y < mid)));
+        }
+        if (lane < nw && rank < k) cand[wave][rank] = make_uint2(mk, mid);
+      }
+    }
+  }
+  // General form: a lane keeps its two best entries (its registers hold ids
+  // in ascending order, so of equal keys the first is the smaller id); a
+  // round is the wave maximum of the lanes' first keys, then the smallest id
+  // among the lanes that hold it, and the owner moves its second entry up.
+  // A lane that has given up both looks again, for the best entries after
+  // the last one it gave up in (key descending, id ascending) order -- rare,
+  // and only that lane's wave waits for it.
   // 2. after one barrier, wave 0 takes the chunk's k best out of the 4 k
   //    wave candidates in LDS the same way.
   // The keys take the logits' place (a key gives its logit back), which
   // keeps the kernel within the registers of six waves per SIMD.
-  uint32_t key[EPT];
+  if (general) {
+    uint32_t key[EPT];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) key[j] = ((live >> j) & 1u) ? fkey(x[j]) : 0u;
-  // the two best entries after (bk, bj) in the order; bk = ~0u: from the top
-  auto best_two = [&](uint32_t lk, int lj, uint32_t& k1, int& j1, uint32_t& k2, int& j2) {
-    k1 = 0u, j1 = 0, k2 = 0u, j2 = 0;
+    for (int j = 0; j < EPT; ++j) key[j] = ((live >> j) & 1u) ? fkey(x[j]) : 0u;
+    // the two best entries after (bk, bj) in the order; bk = ~0u: from the top
+    auto best_two = [&](uint32_t lk, int lj, uint32_t& k1, int& j1, uint32_t& k2, int& j2) {
+      k1 = 0u, j1 = 0, k2 = 0u, j2 = 0;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      // bitwise, not short-circuit: no branches around the comparisons
-      const bool after = (key[j] < lk) | ((key[j] == lk) & (j > lj));
-      const uint32_t kj = after ? key[j] : 0u;
-      const bool first = kj > k1, second = !first && kj > k2;
-      k2 = first ? k1 : (second ? kj : k2);
-      j2 = first ? j1 : (second ? j : j2);
-      k1 = first ? kj : k1;
-      j1 = first ? j : j1;
-    }
-  };
-  uint32_t k1, k2;
-  int j1, j2;
-  best_two(0xffffffffu, -1, k1, j1, k2, j2);
-  for (int r = 0; r < k; ++r) {
-    const uint32_t myid = k1 ? (uint32_t)(c0 + elem_of_rt<T, VEC>(t, j1)) : 0xffffffffu;
-    uint32_t wk;
-    const bool owner = wave_owner(k1, myid, wk);
-    if (wk == 0u) {  // fewer than k logits in the wave
-      if (lane == 0) cand[wave][r] = make_uint2(0u, 0xffffffffu);
-    } else if (owner) {
-      cand[wave][r] = make_uint2(wk, myid);
-      if (k2 != 0u) {
-        k1 = k2, j1 = j2, k2 = 0u;
-      } else {
-        best_two(k1, j1, k1, j1, k2, j2);
+      for (int j = 0; j < EPT; ++j) {
+        // bitwise, not short-circuit: no branches around the comparisons
+        const bool after = (key[j] < lk) | ((key[j] == lk) & (j > lj));
+        const uint32_t kj = after ? key[j] : 0u;
+        const bool first = kj > k1, second = !first && kj > k2;
+        k2 = first ? k1 : (second ? kj : k2);
+        j2 = first ? j1 : (second ? j : j2);
+        k1 = first ? kj : k1;
+        j1 = first ? j : j1;
+      }
+    };
+    uint32_t k1, k2;
+    int j1, j2;
+    best_two(0xffffffffu, -1, k1, j1, k2, j2);
+    for (int r = 0; r < k; ++r) {
+      const uint32_t myid = k1 ? (uint32_t)(c0 + elem_of_rt<T, VEC>(t, j1)) : 0xffffffffu;
+      uint32_t wk;
+      const bool owner = wave_owner(k1, myid, wk);
+      if (wk == 0u) {  // fewer than k logits in the wave
+        if (lane == 0) cand[wave][r] = make_uint2(0u, 0xffffffffu);
+      } else if (owner) {
+        cand[wave][r] = make_uint2(wk, myid);
+        if (k2 != 0u) {
+          k1 = k2, j1 = j2, k2 = 0u;
+        } else {
+          best_two(k1, j1, k1, j1, k2, j2);
+        }
       }
     }
   }
@@ -322,13 +383,14 @@ __global__ __launch_bounds__(CT) void chunk_kernel(const T* __restrict__ logits,
                                                    int32_t* __restrict__ out_id) {
   __shared__ float red_m[CT / 64], red_s[CT / 64];
   __shared__ uint2 cand[CT / 64][KMAX];  // each wave's k best: (key, id)
+  __shared__ uint2 stage[CT / 64][STAGE];  // each wave's logits at or above its threshold
   const int row = blockIdx.x / C, c = blockIdx.x % C;
   if ((long long)(c + 1) * CHUNK <= vocab)
     chunk_body<T, VEC, true>(logits, vocab, C, k, ws_ms, ws_val, ws_id, out_val, out_id, row, c, red_m,
-                             red_s, cand);
+                             red_s, cand, stage);
   else
     chunk_body<T, VEC, false>(logits, vocab, C, k, ws_ms, ws_val, ws_id, out_val, out_id, row, c, red_m,
-                              red_s, cand);
+                              red_s, cand, stage);
 }
 
 __global__ __launch_bounds__(64) void merge_kernel(int C, int k, const float* __restrict__ ws_ms,
