@@ -13,8 +13,11 @@
 // * chunk_kernel: workgroup (row, chunk) reads CHUNK consecutive logits of
 //   its row once (32 per thread, kept in registers) and writes the chunk's
 //   max m_c, its sum s_c of e^(x - m_c), and its k best (value, id), best
-//   first, by rounds of an argmax over the entries still in play (32-bit
-//   order keys, the smallest id among equal keys);
+//   first (32-bit order keys, the smallest id among equal keys): each wave
+//   ranks its logits at or above a threshold that at least k of them reach
+//   (rounds of an argmax over its entries where equal or -inf logits leave
+//   no useful threshold), and each wave's list is then placed by counting
+//   the entries of the other three lists before each of its entries;
 //   (a row of one chunk -- vocabularies up to CHUNK -- is final there:
 //   the chunk writes x - lse and the ids itself and no merge runs);
 // * merge_kernel: one wavefront per row folds the chunks' (m_c, s_c) into
@@ -279,8 +282,6 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
   // A lane that has given up both looks again, for the best entries after
   // the last one it gave up in (key descending, id ascending) order -- rare,
   // and only that lane's wave waits for it.
-  // 2. after one barrier, wave 0 takes the chunk's k best out of the 4 k
-  //    wave candidates in LDS the same way.
   // The keys take the logits' place (a key gives its logit back), which
   // keeps the kernel within the registers of six waves per SIMD.
   if (general) {
@@ -310,7 +311,7 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
       uint32_t wk;
       const bool owner = wave_owner(k1, myid, wk);
       if (wk == 0u) {  // fewer than k logits in the wave
-        if (lane == 0) cand[wave][r] = make_uint2(0u, 0xffffffffu);
+        if (lane == 0) cand[wave][r] = make_uint2(0u, 0xffffffffu - (uint32_t)(wave * KMAX + r));
       } else if (owner) {
         cand[wave][r] = make_uint2(wk, myid);
         if (k2 != 0u) {
@@ -322,8 +323,7 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
     }
   }
   __syncthreads();
-  if (wave != 0) return;
-  // the workgroup's (max, sum), waves in order
+  // the workgroup's (max, sum), waves in order (every wave forms it)
   float mc = red_m[0], sc = red_s[0];
   lse_add(mc, sc, red_m[1], red_s[1]);
   lse_add(mc, sc, red_m[2], red_s[2]);
@@ -337,39 +337,35 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
   // k best, best first, are the row's.
   const bool whole_row = C == 1;
   const float lse = mc + __logf(sc);
-  // wave 0: candidate i = (wave i / k, round i % k), two per lane
-  uint32_t ck[2], cid[2];
-  float cv[2];
+  // 2. each wave places its own list's entries: the chunk-wide place of
+  //    entry p of a wave's list is p plus the number of entries of the other
+  //    three lists before it in the order (each list is sorted, so places
+  //    0 .. k-1 are each taken once); entries placed at k or later drop out.
+  //    Entries standing for nothing (key 0, distinct ids above every token
+  //    id) come after every real one.
+  if (lane < k) {
+    const uint2 me = cand[wave][lane];
+    int place = lane;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int i = lane + 64 * q;
-    ck[q] = 0u, cid[q] = 0xffffffffu, cv[q] = 0.f;
-    if (i < (CT / 64) * k) {
-      const uint2 v = cand[i / k][i % k];
-      ck[q] = v.x, cid[q] = v.y, cv[q] = funkey(v.x);
+    for (int d = 1; d < CT / 64; ++d) {
+      const int w2 = (wave + d) & (CT / 64 - 1);
+#pragma unroll 4
+      for (int q = 0; q < k; ++q) {
+        const uint2 v = cand[w2][q];  // the same entry in every lane
+        place += (int)((v.x > me.x) | ((v.x == me.x) & (v.y < me.y)));
+      }
     }
-  }
-  for (int r = 0; r < k; ++r) {
-    // the lane's best of its two (the larger key, then the smaller id)
-    const bool second = ck[1] > ck[0] || (ck[1] == ck[0] && cid[1] < cid[0]);
-    const uint32_t lk = second ? ck[1] : ck[0], lid = second ? cid[1] : cid[0];
-    const float lv = second ? cv[1] : cv[0];
-    uint32_t gk;
-    const bool owner = wave_owner(lk, lid, gk);
-    if (gk == 0u) {
-      if (lane == 0 && !whole_row) {
-        ws_val[slot * k + r] = -INFINITY;
-        ws_id[slot * k + r] = INT_MAX;
-      }
-    } else if (owner) {
+    if (place < k) {
       if (whole_row) {
-        out_val[(size_t)row * k + r] = lv - lse;
-        out_id[(size_t)row * k + r] = (int32_t)lid;
+        out_val[(size_t)row * k + place] = funkey(me.x) - lse;
+        out_id[(size_t)row * k + place] = (int32_t)me.y;
+      } else if (me.x == 0u) {
+        ws_val[slot * k + place] = -INFINITY;
+        ws_id[slot * k + place] = INT_MAX;
       } else {
-        ws_val[slot * k + r] = lv;
-        ws_id[slot * k + r] = (int32_t)lid;
+        ws_val[slot * k + place] = funkey(me.x);
+        ws_id[slot * k + place] = (int32_t)me.y;
       }
-      if (second) ck[1] = 0u; else ck[0] = 0u;
     }
   }
 }
