@@ -216,8 +216,8 @@ __device__ __forceinline__ void chunk_body(const T* __restrict__ logits, int voc
   const size_t slot = (size_t)row * C + c;
 
   // The chunk's k best (the largest value, then the smallest id), in two
-  // steps without a barrier per round.  Keys are 32-bit order keys; 0 means
-  // nothing (every float's key is larger).
+  // steps with one barrier between them.  Keys are 32-bit order keys; 0
+  // means nothing (every float's key is larger).
   // 1. each wave takes its own k best, cand[wave][0 .. k-1].
   //    Threshold form: the k-th largest of the lanes' maxima, tau, is at most
   //    the wave's k-th largest logit (each of those k lanes holds a logit
